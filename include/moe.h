@@ -1,0 +1,180 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) BF16 Mixture-of-Experts expert path.
+ *
+ * One layer of the path is: router logits -> softmax top-k routing with
+ * expert grouping -> grouped gate-up GEMM with SiLU-mul -> grouped
+ * down-projection carrying the routing weight -> weighted top-k combine with
+ * a sigmoid-gated shared-expert term.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [Issue 3094] vllm.cpp issue #3094, row "BACKEND-ROCM-BF16-MOE", row
+ *       statement: ROCm lacks the BF16 grouped expert GEMMs (plain and
+ *       gate-up + SiLU); numeric contract N1 (GEMM result narrowed to bf16
+ *       before the activation), N2 (routing weight applied before the
+ *       down-projection result is stored), N3 (the reduction must not apply
+ *       the routing weights a second time).
+ *   [PR 509] vllm.cpp PR #509 "feat(rocm): MoE combine/gate ops --
+ *       SharedExpertGate, MoeCombine, MoeCombineGate": What changed (combine
+ *       formulas), Honest gaps (ungrouped softmax router), review comment
+ *       (f32/bf16 arms only, f16 refused with a named message; expert_out is
+ *       the pair-major [T,K,H] bf16 buffer), rework commit (bit-exact combine:
+ *       thread per element, sequential k, one store rounding, no
+ *       contraction), routed_scale commit (one multiply on the finished routed
+ *       sum before the shared add).
+ *   [PR 523] keep-quant grouped expert GEMM, What changed / Honest gaps:
+ *       grouping over expert ids; capture-safe scratch that never
+ *       reallocates during reuse.
+ *
+ * Conventions common to every call
+ *   - All data pointers are DEVICE pointers (hipMalloc'd or equivalent) of the
+ *     current HIP device, owned by the caller. The library never allocates or
+ *     frees, never synchronises, and keeps no state beyond a thread-local
+ *     error string and a per-device "checked" flag.
+ *   - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
+ *   - All tensors are dense row-major with the shapes given; base pointers of
+ *     bf16/f32 tensors read or written with 16-byte vectors must be 16-byte
+ *     aligned (stated per argument).
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only
+ *     enqueues work on it and returns; it is legal inside hipGraph capture
+ *     once moe_init() has run outside capture.
+ *   - Validation happens on the host before any launch. On failure the call
+ *     returns a non-zero moe_status, launches nothing, leaves the outputs
+ *     untouched and records a message naming the call, the argument and the
+ *     missing piece (moe_last_error). A launch error maps to MOE_E_HIP.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - A call with zero tokens (T == 0 or P == 0) returns MOE_OK and does
+ *     nothing.
+ *   - Limits: 1 <= K <= E, E <= 1024, K <= 32, H and I multiples of 8,
+ *     T*K < 2^31, T*max(H,I,E) < 2^31 elements per tensor row block.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_INVALID = 1,   /* null/misaligned pointer, non-finite scalar, bad flag */
+  MOE_E_DTYPE = 2,     /* dtype arm not implemented (f16) or unknown        */
+  MOE_E_SHAPE = 3,     /* a dimension outside the limits above              */
+  MOE_E_WORKSPACE = 4, /* workspace smaller than the query returned          */
+  MOE_E_HIP = 5        /* a HIP runtime error (wrong device arch, launch)    */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_F16 = 2          /* exists only so that it can be refused by name */
+} moe_dtype;
+
+/* hipStream_t, passed as an opaque pointer so this header needs no HIP headers. */
+typedef void* moe_stream_t;
+
+/* Message of the last failed call on this thread ("" if none). Never NULL. */
+const char* moe_last_error(void);
+
+/* Checks that the current device is gfx950 and loads the code objects. Call
+ * once per device before any hipGraph capture; the other calls do it on
+ * first use. Returns MOE_E_HIP (with a message) on another architecture. */
+moe_status moe_init(void);
+
+/*
+ * Router / gate logits helper (not a contract step; the router itself is the
+ * ungrouped softmax top-k of [PR 509] Honest gaps).
+ *   out[t,n] = f32( sum_h x[t,h] * w[n,h] )  (+ bias[n] as one f32 add)
+ *   x    bf16 [T,H], 16-byte aligned          w    bf16 [N,H], 16-byte aligned
+ *   bias f32 [N] or NULL                      out  f32 [T,N]
+ * The sum is an f32 MFMA accumulation in the kernel's own order. N >= 1
+ * (N = E for the router, N = 1 for the shared-expert gate logit).
+ */
+moe_status moe_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
+                             const float* bias, float* out, moe_stream_t stream);
+
+/* Bytes of device workspace moe_route needs (currently 0: pass NULL/0). */
+size_t moe_route_workspace_bytes(int T, int E, int K);
+
+/*
+ * Softmax top-k routing with renormalisation and stable expert grouping
+ * ([PR 509] Honest gaps: ungrouped softmax; [PR 523]: grouping by expert id).
+ *   logits         f32 [T,E] (read only)
+ *   topk_ids       int32 [T,K]: the K largest logits per token, descending,
+ *                  ties to the lower expert id, NaN ranked as -inf
+ *   topk_w         f32 [T,K]: w_k = e_k / (((e_0 + e_1) + ...) + e_{K-1}),
+ *                  e_k = exp(l_k - l_0) with the library's bit-reproducible
+ *                  f32 exp (Cody-Waite reduction + degree-7 Taylor)
+ *   expert_offsets int32 [E+1]: offsets[e] = number of pairs routed to
+ *                  experts below e; offsets[E] = T*K
+ *   sorted_pairs   int32 [T*K]: pair indices p = t*K + k grouped by expert,
+ *                  increasing p within an expert
+ *   ws, ws_bytes   workspace of at least moe_route_workspace_bytes(T,E,K)
+ * Results are bit-identical run to run (no atomics decide an order).
+ */
+moe_status moe_route(const float* logits, int T, int E, int K, int32_t* topk_ids,
+                     float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                     void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Grouped gate-up GEMM with SiLU-mul ([Issue 3094] row statement, N1).
+ * For sorted row q of expert e (p = sorted_pairs[q], token t = p / K):
+ *   gu[j]    = bf16( f32( x[t] . w_gu[e,j] ) )          j < 2I   (N1)
+ *   act[q,i] = bf16( silu(gu[i]) * gu[I+i] ),  silu(g) = g / (1 + exp(-g))
+ *   x      bf16 [T,H], 16-byte aligned
+ *   w_gu   bf16 [E,2I,H] (gate rows [0,I), up rows [I,2I)), 16-byte aligned
+ *   sorted_pairs, expert_offsets  as produced by moe_route(T, E, K); both
+ *          NULL means identity rows (E must be 1 and K 1: a dense expert,
+ *          e.g. the shared expert)
+ *   act    bf16 [T*K, I] in sorted order, 16-byte aligned
+ * Experts with no rows cost nothing. f32 accumulation on MFMA.
+ */
+moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w_gu,
+                                        int E, int I, const int32_t* sorted_pairs,
+                                        const int32_t* expert_offsets, int K, uint16_t* act,
+                                        moe_stream_t stream);
+
+/*
+ * Grouped down-projection with the routing weight in the epilogue
+ * ([Issue 3094] row statement, N2 and N3).
+ *   y = f32( act[q] . w_d[e,h] );  expert_out[p,h] = bf16( y * pair_w[p] )
+ *   stored at pair row p = sorted_pairs[q], so expert_out is [T,K,H].
+ *   act    bf16 [P,I] in sorted order, 16-byte aligned
+ *   w_d    bf16 [E,H,I], 16-byte aligned
+ *   sorted_pairs, expert_offsets  from moe_route, or both NULL (identity, E=1)
+ *   pair_w f32 [P] (= topk_w viewed flat) or NULL for no multiply
+ *   expert_out bf16 [P,H], 16-byte aligned
+ */
+moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const uint16_t* w_d, int E,
+                                 int H, const int32_t* sorted_pairs,
+                                 const int32_t* expert_offsets, const float* pair_w,
+                                 uint16_t* expert_out, moe_stream_t stream);
+
+/*
+ * Weighted top-k combine with routed scale and an optional (gated) shared
+ * term ([PR 509] What changed, rework and routed_scale commits). Per (t,h),
+ * f32, each operation rounded on its own (no contraction):
+ *   acc = +0; for k = 0..K-1: v = expert_out[t,k,h]; if (topk_w) v = topk_w[t,k]*v;
+ *             acc = acc + v
+ *   acc = acc * routed_scale
+ *   if (shared): s = shared[t,h]; if (gate_logit) s = f32(bf16(sigmoid(gate_logit[t]) * s));
+ *                acc = acc + s
+ *   out[t,h] = bf16(acc) or acc (by out_dt)
+ *   expert_out eo_dt [T,K,H]; topk_w f32 [T,K] or NULL (weights already applied);
+ *   shared sh_dt [T,H] or NULL; gate_logit f32 [T] or NULL (ungated shared add);
+ *   out out_dt [T,H]. eo_dt, sh_dt, out_dt in {MOE_F32, MOE_BF16}; MOE_F16 is
+ *   refused with MOE_E_DTYPE. Tensor base pointers 16-byte aligned.
+ *   routed_scale must be finite (1.0 is the neutral value).
+ */
+moe_status moe_combine_gate(const void* expert_out, moe_dtype eo_dt, int T, int K, int H,
+                            const float* topk_w, float routed_scale, const void* shared,
+                            moe_dtype sh_dt, const float* gate_logit, void* out,
+                            moe_dtype out_dt, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

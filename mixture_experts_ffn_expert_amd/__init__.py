@@ -1,0 +1,293 @@
+"""Python binding of libmoe.so, the MI355X (gfx950) BF16 MoE expert path.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libmoe.so (C ABI in include/moe.h). torch supplies device memory and the
+current stream. The binding raises ``MoeError`` with the library's message
+when a call is refused, and ``RuntimeError`` when the library is not built:
+there is no fallback path.
+
+Functions (same names as the C ABI):
+  moe_router_logits(x, w, bias=None, out=None)                -> f32 [T, N]
+  moe_route(logits, K, ...)                                   -> ids, w, offsets, sorted_pairs
+  moe_grouped_gemm_gateup_silu(x, w_gu, sorted_pairs, expert_offsets, K, act=None)
+  moe_grouped_gemm_down(act, w_d, sorted_pairs, expert_offsets, pair_w, expert_out=None)
+  moe_combine_gate(expert_out, T, K, topk_w=None, routed_scale=1.0, shared=None,
+                   gate_logit=None, out=None, out_dtype=torch.bfloat16)
+plus ``moe_layer`` which enqueues one whole layer.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MoeError", "load", "lib_path", "moe_init", "moe_router_logits", "moe_route",
+    "moe_route_workspace_bytes", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
+    "moe_combine_gate", "moe_layer", "MOE_F32", "MOE_BF16", "MOE_F16", "SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmoe.so")
+_lib = None
+
+MOE_F32, MOE_BF16, MOE_F16 = 0, 1, 2
+STATUS = {0: "MOE_OK", 1: "MOE_E_INVALID", 2: "MOE_E_DTYPE", 3: "MOE_E_SHAPE",
+          4: "MOE_E_WORKSPACE", 5: "MOE_E_HIP"}
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_st = ctypes.c_int
+SYMBOLS = {
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_init": (_st, []),
+    "moe_router_logits": (_st, [_p, _i, _i, _p, _i, _p, _p, _p]),
+    "moe_route_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
+    "moe_route": (_st, [_p, _i, _i, _i, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
+    "moe_grouped_gemm_gateup_silu": (_st, [_p, _i, _i, _p, _i, _i, _p, _p, _i, _p, _p]),
+    "moe_grouped_gemm_down": (_st, [_p, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p]),
+    "moe_combine_gate": (_st, [_p, _i, _i, _i, _i, _p, ctypes.c_float, _p, _i, _p, _p, _i, _p]),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libmoe.so (built by ``__graft_entry__.build()``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python mixture_experts_ffn_expert_amd/build.py` first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name, (res, args) in SYMBOLS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoeError(status, load().moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise MoeError(2, f"{name} dtype {t.dtype} unsupported (expected {dtype})")
+    if not t.is_cuda:
+        raise MoeError(1, f"{name} must be a device (cuda/hip) tensor")
+    if not t.is_contiguous():
+        raise MoeError(1, f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise MoeError(3, f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise MoeError(3, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _dt_code(dtype):
+    import torch
+    if dtype == torch.float32:
+        return MOE_F32
+    if dtype == torch.bfloat16:
+        return MOE_BF16
+    if dtype == torch.float16:
+        return MOE_F16
+    raise MoeError(2, f"dtype {dtype} unsupported (f32 or bf16)")
+
+
+def moe_init():
+    _check(load().moe_init())
+
+
+def moe_router_logits(x, w, bias=None, out=None, stream=None):
+    import torch
+    _need(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    _need(w, "w", torch.bfloat16, 2)
+    N = w.shape[0]
+    if w.shape[1] != H:
+        raise MoeError(3, f"w must be [N, {H}], got {tuple(w.shape)}")
+    if bias is not None:
+        _need(bias, "bias", torch.float32, shape=(N,))
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.float32, shape=(T, N))
+    _check(load().moe_router_logits(_ptr(x), T, H, _ptr(w), N, _ptr(bias), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_route_workspace_bytes(T, E, K):
+    return int(load().moe_route_workspace_bytes(T, E, K))
+
+
+def moe_route(logits, K, topk_ids=None, topk_w=None, expert_offsets=None, sorted_pairs=None,
+              workspace=None, stream=None):
+    import torch
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    dev = logits.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if expert_offsets is None:
+        expert_offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    if sorted_pairs is None:
+        sorted_pairs = torch.empty((T * K,), dtype=torch.int32, device=dev)
+    _need(topk_ids, "topk_ids", torch.int32, shape=(T, K))
+    _need(topk_w, "topk_w", torch.float32, shape=(T, K))
+    _need(expert_offsets, "expert_offsets", torch.int32, shape=(E + 1,))
+    _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * K,))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().moe_route(_ptr(logits), T, E, K, _ptr(topk_ids), _ptr(topk_w),
+                            _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(workspace), ws_bytes,
+                            _stream(stream)))
+    return topk_ids, topk_w, expert_offsets, sorted_pairs
+
+
+def moe_grouped_gemm_gateup_silu(x, w_gu, sorted_pairs, expert_offsets, K, act=None, stream=None):
+    import torch
+    _need(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    _need(w_gu, "w_gu", torch.bfloat16, 3)
+    E, twoI, Hw = w_gu.shape
+    if Hw != H or twoI % 2:
+        raise MoeError(3, f"w_gu must be [E, 2I, {H}], got {tuple(w_gu.shape)}")
+    I = twoI // 2
+    if sorted_pairs is not None:
+        _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * K,))
+    if expert_offsets is not None:
+        _need(expert_offsets, "expert_offsets", torch.int32, shape=(E + 1,))
+    if act is None:
+        act = torch.empty((T * K, I), dtype=torch.bfloat16, device=x.device)
+    _need(act, "act", torch.bfloat16, shape=(T * K, I))
+    _check(load().moe_grouped_gemm_gateup_silu(_ptr(x), T, H, _ptr(w_gu), E, I, _ptr(sorted_pairs),
+                                               _ptr(expert_offsets), K, _ptr(act), _stream(stream)))
+    return act
+
+
+def moe_grouped_gemm_down(act, w_d, sorted_pairs, expert_offsets, pair_w, expert_out=None,
+                          stream=None):
+    import torch
+    _need(act, "act", torch.bfloat16, 2)
+    P, I = act.shape
+    _need(w_d, "w_d", torch.bfloat16, 3)
+    E, H, Iw = w_d.shape
+    if Iw != I:
+        raise MoeError(3, f"w_d must be [E, H, {I}], got {tuple(w_d.shape)}")
+    if sorted_pairs is not None:
+        _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(P,))
+    if expert_offsets is not None:
+        _need(expert_offsets, "expert_offsets", torch.int32, shape=(E + 1,))
+    if pair_w is not None:
+        _need(pair_w, "pair_w", torch.float32)
+        if pair_w.numel() != P:
+            raise MoeError(3, f"pair_w must hold {P} weights, got {pair_w.numel()}")
+    if expert_out is None:
+        expert_out = torch.empty((P, H), dtype=torch.bfloat16, device=act.device)
+    _need(expert_out, "expert_out", torch.bfloat16, shape=(P, H))
+    _check(load().moe_grouped_gemm_down(_ptr(act), P, I, _ptr(w_d), E, H, _ptr(sorted_pairs),
+                                        _ptr(expert_offsets), _ptr(pair_w), _ptr(expert_out),
+                                        _stream(stream)))
+    return expert_out
+
+
+def moe_combine_gate(expert_out, T, K, topk_w=None, routed_scale=1.0, shared=None,
+                     gate_logit=None, out=None, out_dtype=None, stream=None):
+    import torch
+    if not isinstance(expert_out, torch.Tensor):
+        raise TypeError("expert_out must be a torch.Tensor")
+    eo_dt = _dt_code(expert_out.dtype)
+    H = expert_out.numel() // max(1, T * K)
+    if T * K * H != expert_out.numel():
+        raise MoeError(3, f"expert_out holds {expert_out.numel()} values, not T*K*H")
+    _need(expert_out, "expert_out", expert_out.dtype)
+    sh_dt = MOE_BF16
+    if shared is not None:
+        sh_dt = _dt_code(shared.dtype)
+        _need(shared, "shared", shared.dtype)
+        if shared.numel() != T * H:
+            raise MoeError(3, f"shared must hold T*H = {T * H} values")
+    if topk_w is not None:
+        _need(topk_w, "topk_w", torch.float32)
+        if topk_w.numel() != T * K:
+            raise MoeError(3, f"topk_w must hold T*K = {T * K} values")
+    if gate_logit is not None:
+        _need(gate_logit, "gate_logit", torch.float32)
+        if gate_logit.numel() != T:
+            raise MoeError(3, f"gate_logit must hold T = {T} values")
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype or torch.bfloat16, device=expert_out.device)
+    out_dt = _dt_code(out.dtype)
+    _need(out, "out", out.dtype)
+    _check(load().moe_combine_gate(_ptr(expert_out), eo_dt, T, K, H, _ptr(topk_w),
+                                   float(routed_scale), _ptr(shared), sh_dt, _ptr(gate_logit),
+                                   _ptr(out), out_dt, _stream(stream)))
+    return out
+
+
+def moe_layer(x, w_r, w_gu, w_d, K, router_bias=None, w_gu_s=None, w_d_s=None, w_g=None,
+              bufs=None, stream=None):
+    """Enqueue one MoE layer: logits, route, gate-up, down, (shared), combine.
+
+    ``bufs`` (dict) may hold preallocated outputs/intermediates under the keys
+    logits, ids, w, offsets, sorted, act, expert_out, sd_act, sd, gl, out; the
+    dict is filled with everything produced. Returns the bf16 [T, H] output.
+    """
+    import torch
+    T, H = x.shape
+    E = w_r.shape[0]
+    I = w_gu.shape[1] // 2
+    b = {} if bufs is None else bufs
+    dev = x.device
+
+    def buf(key, shape, dtype):
+        if b.get(key) is None:
+            b[key] = torch.empty(shape, dtype=dtype, device=dev)
+        return b[key]
+
+    logits = moe_router_logits(x, w_r, router_bias, buf("logits", (T, E), torch.float32), stream)
+    ids, w, off, sp = moe_route(logits, K, buf("ids", (T, K), torch.int32),
+                                buf("w", (T, K), torch.float32),
+                                buf("offsets", (E + 1,), torch.int32),
+                                buf("sorted", (T * K,), torch.int32), stream=stream)
+    act = moe_grouped_gemm_gateup_silu(x, w_gu, sp, off, K, buf("act", (T * K, I), torch.bfloat16),
+                                       stream)
+    eo = moe_grouped_gemm_down(act, w_d, sp, off, w, buf("expert_out", (T * K, H), torch.bfloat16),
+                               stream)
+    sd = gl = None
+    if w_gu_s is not None:
+        Is = w_gu_s.shape[0] // 2
+        sa = moe_grouped_gemm_gateup_silu(x, w_gu_s.view(1, 2 * Is, H), None, None, 1,
+                                          buf("sd_act", (T, Is), torch.bfloat16), stream)
+        sd = moe_grouped_gemm_down(sa, w_d_s.view(1, H, Is), None, None, None,
+                                   buf("sd", (T, H), torch.bfloat16), stream)
+        gl = moe_router_logits(x, w_g.view(1, H), None, buf("gl", (T, 1), torch.float32), stream)
+    return moe_combine_gate(eo, T, K, None, 1.0, sd, gl, buf("out", (T, H), torch.bfloat16),
+                            stream=stream)

@@ -1,0 +1,259 @@
+// api.cpp -- the C ABI of the MoE expert path (declared in include/moe.h):
+// host-side argument validation, refusals with named messages, then one
+// stream-ordered launch sequence per call. No allocation, no synchronisation.
+//
+// Refusal rule: vllm.cpp PR #509 review comment -- only the f32 and bf16
+// arms exist, and anything else (f16) is refused with a message that names
+// the missing piece instead of being reinterpreted.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_err() { g_err[0] = 0; }
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_dev_mu;
+int g_dev_state[kMaxDevices] = {0};  // 0 unknown, 1 gfx950, 2 other
+
+moe_status check_device(const char* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_E_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_E_HIP, "%s: device index %d out of range", fn, dev);
+  int st;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    st = g_dev_state[dev];
+  }
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(MOE_E_HIP, "%s: hipGetDeviceProperties failed: %s", fn, hipGetErrorString(e));
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    g_dev_state[dev] = st;
+    if (st == 2)
+      return fail(MOE_E_HIP, "%s: device %d is %s; this library is built for gfx950 (MI355X) only",
+                  fn, dev, prop.gcnArchName);
+  }
+  if (st == 2) return fail(MOE_E_HIP, "%s: device %d is not gfx950 (MI355X)", fn, dev);
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+const char* dtype_name(moe_dtype d) {
+  switch (d) {
+    case MOE_F32: return "f32";
+    case MOE_BF16: return "bf16";
+    case MOE_F16: return "f16";
+  }
+  return "unknown";
+}
+
+moe_status check_dtype(const char* fn, const char* arg, moe_dtype d) {
+  if (d == MOE_F32 || d == MOE_BF16) return MOE_OK;
+  return fail(MOE_E_DTYPE, "%s: %s dtype %s unsupported (only the f32 and bf16 arms exist)", fn, arg,
+              dtype_name(d));
+}
+
+#define REQUIRE_PTR(fn, p)                                                          \
+  do {                                                                              \
+    if ((p) == nullptr) return fail(MOE_E_INVALID, "%s: %s is NULL", fn, #p);       \
+    if (!aligned16(p)) return fail(MOE_E_INVALID, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+#define REQUIRE_NONNULL(fn, p)                                                      \
+  do {                                                                              \
+    if ((p) == nullptr) return fail(MOE_E_INVALID, "%s: %s is NULL", fn, #p);       \
+  } while (0)
+
+moe_status hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(MOE_E_HIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+bool fits_i32(long long v) { return v >= 0 && v < (1LL << 31); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status moe_init(void) {
+  clear_err();
+  return check_device("moe_init");
+}
+
+moe_status moe_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
+                             const float* bias, float* out, moe_stream_t stream) {
+  const char* fn = "moe_router_logits";
+  clear_err();
+  if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
+  if (H <= 0 || H % 8) return fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);
+  if (N < 1) return fail(MOE_E_SHAPE, "%s: N=%d must be >= 1", fn, N);
+  if (!fits_i32((long long)T * H) || !fits_i32((long long)T * N) || !fits_i32((long long)N * H))
+    return fail(MOE_E_SHAPE, "%s: T*H, T*N or N*H exceeds 2^31 elements", fn);
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(fn, x);
+  REQUIRE_PTR(fn, w);
+  REQUIRE_NONNULL(fn, out);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_logits(x, T, H, w, N, bias, out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_route_workspace_bytes(int T, int E, int K) {
+  (void)T;
+  (void)E;
+  (void)K;
+  return 0;
+}
+
+moe_status moe_route(const float* logits, int T, int E, int K, int32_t* topk_ids, float* topk_w,
+                     int32_t* expert_offsets, int32_t* sorted_pairs, void* ws, size_t ws_bytes,
+                     moe_stream_t stream) {
+  const char* fn = "moe_route";
+  clear_err();
+  if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
+  if (E < 1 || E > kMaxE) return fail(MOE_E_SHAPE, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if (K < 1 || K > E || K > kMaxK)
+    return fail(MOE_E_SHAPE, "%s: K=%d outside [1, min(E=%d, %d)]", fn, K, E, kMaxK);
+  if (!fits_i32((long long)T * E) || !fits_i32((long long)T * K))
+    return fail(MOE_E_SHAPE, "%s: T*E or T*K exceeds 2^31", fn);
+  if (ws_bytes < moe_route_workspace_bytes(T, E, K))
+    return fail(MOE_E_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, ws_bytes,
+                moe_route_workspace_bytes(T, E, K));
+  (void)ws;
+  REQUIRE_NONNULL(fn, expert_offsets);
+  if (T == 0) return MOE_OK;  // nothing routed; no output is written
+  REQUIRE_NONNULL(fn, logits);
+  REQUIRE_NONNULL(fn, topk_ids);
+  REQUIRE_NONNULL(fn, topk_w);
+  REQUIRE_NONNULL(fn, sorted_pairs);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_route(logits, T, E, K, topk_ids, topk_w, expert_offsets,
+                                          sorted_pairs, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w_gu,
+                                        int E, int I, const int32_t* sorted_pairs,
+                                        const int32_t* expert_offsets, int K, uint16_t* act,
+                                        moe_stream_t stream) {
+  const char* fn = "moe_grouped_gemm_gateup_silu";
+  clear_err();
+  if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
+  if (H <= 0 || H % 8) return fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);
+  if (I <= 0 || I % 8) return fail(MOE_E_SHAPE, "%s: I=%d must be a positive multiple of 8", fn, I);
+  if (E < 1 || E > kMaxE) return fail(MOE_E_SHAPE, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if (K < 1 || K > E || K > kMaxK)
+    return fail(MOE_E_SHAPE, "%s: K=%d outside [1, min(E=%d, %d)]", fn, K, E, kMaxK);
+  if ((sorted_pairs == nullptr) != (expert_offsets == nullptr))
+    return fail(MOE_E_INVALID, "%s: sorted_pairs and expert_offsets must both be set or both NULL",
+                fn);
+  if (sorted_pairs == nullptr && (E != 1 || K != 1))
+    return fail(MOE_E_INVALID, "%s: identity rows (NULL sorted_pairs) need E=1 and K=1, got E=%d K=%d",
+                fn, E, K);
+  if (!fits_i32((long long)T * K) || !fits_i32((long long)T * H) ||
+      !fits_i32((long long)T * K * I) || !fits_i32(2LL * I * H))
+    return fail(MOE_E_SHAPE, "%s: a tensor exceeds 2^31 elements per expert/row block", fn);
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(fn, x);
+  REQUIRE_PTR(fn, w_gu);
+  REQUIRE_PTR(fn, act);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_gateup_silu(x, T, H, w_gu, E, I, sorted_pairs, expert_offsets,
+                                                K, act, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const uint16_t* w_d, int E,
+                                 int H, const int32_t* sorted_pairs,
+                                 const int32_t* expert_offsets, const float* pair_w,
+                                 uint16_t* expert_out, moe_stream_t stream) {
+  const char* fn = "moe_grouped_gemm_down";
+  clear_err();
+  if (P < 0) return fail(MOE_E_SHAPE, "%s: P=%d is negative", fn, P);
+  if (H <= 0 || H % 8) return fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);
+  if (I <= 0 || I % 8) return fail(MOE_E_SHAPE, "%s: I=%d must be a positive multiple of 8", fn, I);
+  if (E < 1 || E > kMaxE) return fail(MOE_E_SHAPE, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if ((sorted_pairs == nullptr) != (expert_offsets == nullptr))
+    return fail(MOE_E_INVALID, "%s: sorted_pairs and expert_offsets must both be set or both NULL",
+                fn);
+  if (sorted_pairs == nullptr && E != 1)
+    return fail(MOE_E_INVALID, "%s: identity rows (NULL sorted_pairs) need E=1, got E=%d", fn, E);
+  if (!fits_i32((long long)P * I) || !fits_i32((long long)P * H) || !fits_i32((long long)H * I))
+    return fail(MOE_E_SHAPE, "%s: a tensor exceeds 2^31 elements per expert/row block", fn);
+  if (P == 0) return MOE_OK;
+  REQUIRE_PTR(fn, act);
+  REQUIRE_PTR(fn, w_d);
+  REQUIRE_PTR(fn, expert_out);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_down(act, P, I, w_d, E, H, sorted_pairs, expert_offsets,
+                                         pair_w, expert_out, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_combine_gate(const void* expert_out, moe_dtype eo_dt, int T, int K, int H,
+                            const float* topk_w, float routed_scale, const void* shared,
+                            moe_dtype sh_dt, const float* gate_logit, void* out,
+                            moe_dtype out_dt, moe_stream_t stream) {
+  const char* fn = "moe_combine_gate";
+  clear_err();
+  moe_status st = check_dtype(fn, "expert_out", eo_dt);
+  if (st != MOE_OK) return st;
+  if (shared != nullptr) {
+    st = check_dtype(fn, "shared", sh_dt);
+    if (st != MOE_OK) return st;
+  }
+  st = check_dtype(fn, "out", out_dt);
+  if (st != MOE_OK) return st;
+  if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
+  if (K < 1 || K > kMaxK) return fail(MOE_E_SHAPE, "%s: K=%d outside [1, %d]", fn, K, kMaxK);
+  if (H <= 0 || H % 8) return fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);
+  if (!fits_i32((long long)T * K * H))
+    return fail(MOE_E_SHAPE, "%s: T*K*H exceeds 2^31 elements", fn);
+  if (!std::isfinite(routed_scale))
+    return fail(MOE_E_INVALID, "%s: routed_scale is not finite", fn);
+  if (gate_logit != nullptr && shared == nullptr)
+    return fail(MOE_E_INVALID, "%s: gate_logit given without a shared term", fn);
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(fn, expert_out);
+  REQUIRE_PTR(fn, out);
+  if (shared != nullptr && !aligned16(shared))
+    return fail(MOE_E_INVALID, "%s: shared is not 16-byte aligned", fn);
+  st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_combine(expert_out, eo_dt == MOE_BF16, T, K, H, topk_w,
+                                            routed_scale, shared, sh_dt == MOE_BF16, gate_logit,
+                                            out, out_dt == MOE_BF16,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,29 @@
+// launch.h -- internal launchers of the MoE expert-path kernels (not part of
+// the C ABI; the C ABI validates its arguments and then calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// route.hip
+hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w,
+                        int32_t* offsets, int32_t* sorted, hipStream_t s);
+
+// gemm.hip
+hipError_t launch_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w_gu, int E, int I,
+                              const int32_t* sorted, const int32_t* offsets, int K, uint16_t* act,
+                              hipStream_t s);
+hipError_t launch_down(const uint16_t* act, int P, int I, const uint16_t* w_d, int E, int H,
+                       const int32_t* sorted, const int32_t* offsets, const float* pair_w,
+                       uint16_t* expert_out, hipStream_t s);
+hipError_t launch_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
+                         const float* bias, float* out, hipStream_t s);
+
+// combine.hip; dtype codes: 0 = f32, 1 = bf16
+hipError_t launch_combine(const void* eo, int eo_bf16, int T, int K, int H, const float* topk_w,
+                          float routed_scale, const void* shared, int sh_bf16,
+                          const float* gate_logit, void* out, int out_bf16, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,193 @@
+// route.hip -- softmax top-k routing and stable expert grouping on gfx950.
+//
+// Router: the ungrouped softmax top-k with renormalisation that vllm.cpp
+// PR #509 ("MoE combine/gate ops", Honest gaps) names as the covered router
+// form. Grouping: the per-expert row grouping the grouped expert GEMMs run
+// over (issue #3094 row statement; PR #523 What changed, grouped over expert
+// ids).
+//
+// Kernel 1 (topk_kernel): one wavefront per token. Lane l holds logits
+//   e = l + 64*j. K rounds of a wavefront arg-max over (value desc, id asc)
+//   pick the experts; lane k keeps the k-th value, computes e_k = exp(l_k -
+//   l_0), every lane forms the same sequential f32 sum, lane k divides.
+// Kernel 2 (group_kernel): one workgroup of 8 waves. Wave w owns a
+//   contiguous segment of pairs. (i) per-wave expert histogram in LDS,
+//   (ii) exclusive scan over experts of the totals and per-wave bases,
+//   (iii) each wave walks its segment in order, 64 pairs at a time, ranks
+//   equal experts inside the 64 by ballots, and scatters. No atomic decides
+//   an order, so the permutation is the stable one and is reproducible.
+#include "device_math.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxPerLane = kMaxE / 64;
+
+// a better than b: larger value, then lower id.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int K, int32_t* __restrict__ ids,
+                                                   float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave leaves together
+  const float* row = logits + (size_t)t * E;
+  const int nper = (E + 63) >> 6;
+  float v[kMaxPerLane];
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    int e = lane + 64 * j;
+    float x = -__builtin_inff();
+    if (j < nper && e < E) {
+      x = row[e];
+      if (x != x) x = -__builtin_inff();  // NaN ranks as -inf
+    }
+    v[j] = x;
+  }
+  uint32_t taken = 0;
+  float my_val = 0.0f;  // lane k keeps the k-th selected value
+  int my_id = 0;
+  float top = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;  // sentinel: loses every tie against a real id
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      int e = lane + 64 * j;
+      if (j < nper && e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      float ov = __shfl_xor(bv, m);
+      int oi = __shfl_xor(bi, m);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    // the owner lane marks the winner as taken
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (k == 0) top = bv;
+    if (lane == k) {
+      my_val = bv;
+      my_id = bi;
+    }
+  }
+  // renormalised weights: e_k = exp(l_k - l_0), S = ((e_0 + e_1) + ...), w_k = e_k / S
+  float ek = 0.0f;
+  {
+#pragma clang fp contract(off)
+    float d = my_val - top;
+    ek = exp_cw(d);
+  }
+  float S = __shfl(ek, 0);
+  for (int k = 1; k < K; ++k) {
+#pragma clang fp contract(off)
+    S = S + __shfl(ek, k);
+  }
+  if (lane < K) {
+    ids[(size_t)t * K + lane] = my_id;
+    w[(size_t)t * K + lane] = __fdiv_rn(ek, S);
+  }
+}
+
+constexpr int kGroupWaves = 8;
+
+__global__ __launch_bounds__(kGroupWaves * 64) void group_kernel(const int32_t* __restrict__ ids,
+                                                                 int P, int E,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ sorted) {
+  __shared__ int cur[kGroupWaves][kMaxE];  // per-wave counts, then per-wave cursors
+  __shared__ int wave_tot[kGroupWaves * 64 / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < kGroupWaves * kMaxE; i += blockDim.x) (&cur[0][0])[i] = 0;
+  __syncthreads();
+
+  const int seg = (P + kGroupWaves - 1) / kGroupWaves;
+  const int beg = min(P, wave * seg);
+  const int end = min(P, beg + seg);
+  // (i) per-wave histogram (counts commute, so LDS atomics are fine here)
+  for (int p = beg + lane; p < end; p += 64) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cur[wave][e], 1);
+  }
+  __syncthreads();
+
+  // (ii) totals per expert and their exclusive scan; thread i owns experts
+  // [i*per, (i+1)*per) in order.
+  const int nthreads = kGroupWaves * 64;
+  const int per = (E + nthreads - 1) / nthreads;
+  const int e0 = min(E, tid * per);
+  const int e1 = min(E, e0 + per);
+  int local = 0;
+  for (int e = e0; e < e1; ++e)
+    for (int w = 0; w < kGroupWaves; ++w) local += cur[w][e];
+  // inclusive scan of `local` across the block
+  int incl = local;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    int o = __shfl_up(incl, m);
+    if (lane >= m) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int wave_base = 0;
+  for (int w = 0; w < wave; ++w) wave_base += wave_tot[w];
+  int run = wave_base + incl - local;  // exclusive prefix of this thread's first expert
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = run;
+    int c = run;
+    for (int w = 0; w < kGroupWaves; ++w) {
+      int n = cur[w][e];
+      cur[w][e] = c;  // cursor of wave w for expert e
+      c += n;
+    }
+    run = c;
+  }
+  if (tid == 0) offsets[E] = P;
+  __syncthreads();
+
+  // (iii) in-order stable scatter; ranks inside each group of 64 by ballots
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  for (int base = beg; base < end; base += 64) {
+    const int p = base + lane;
+    int e = (p < end) ? ids[p] : 0;
+    const bool valid = p < end && (unsigned)e < (unsigned)E;  // ids come from topk_kernel
+    if (!valid) e = 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      uint64_t m = __ballot(valid && ((e >> b) & 1));
+      peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(peers & below);
+    int pos = 0;
+    if (valid) pos = cur[wave][e] + rank;
+    __builtin_amdgcn_wave_barrier();
+    // the highest lane of each peer group advances the cursor
+    const bool last = valid && ((peers >> lane) == 1ull);
+    if (last) cur[wave][e] = pos + 1;
+    __builtin_amdgcn_wave_barrier();
+    if (valid) sorted[pos] = p;
+  }
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w,
+                        int32_t* offsets, int32_t* sorted, hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupWaves * 64), 0, s, ids, T * K, E, offsets,
+                     sorted);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -22,3 +22,17 @@ def gpu_lib():
     import mixture_experts_ffn_expert_amd as moe
     moe.load()
     return moe
+
+
+_INPUTS = {}
+
+
+def cached_inputs(n, **kw):
+    """Workload inputs generated once per test session (they are large)."""
+    import workloads
+    key = (n, tuple(sorted(kw.items())))
+    if key not in _INPUTS:
+        if len(_INPUTS) >= 2:          # keep host memory bounded
+            _INPUTS.pop(next(iter(_INPUTS)))
+        _INPUTS[key] = workloads.make_inputs(n, **kw)
+    return _INPUTS[key]

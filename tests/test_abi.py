@@ -1,0 +1,160 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+symbol, and refuses bad arguments before touching the device.
+
+No call here reaches a kernel launch: every argument set is rejected by host
+validation (or, on a machine without a GPU, by the device check).
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import mixture_experts_ffn_expert_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+A = ctypes.c_void_p(0x10000)      # aligned, never dereferenced (refused first)
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(moe.SYMBOLS), (names, sorted(moe.SYMBOLS))
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.lib_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (moe_[a-z_0-9]+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        getattr(lib, n)
+
+
+def test_no_torch_types_in_the_abi():
+    txt = open(HEADER).read()
+    assert "torch" not in txt.lower().replace("torch types", "")
+    assert "extern \"C\"" in txt
+
+
+def _err(lib):
+    return lib.moe_last_error().decode()
+
+
+def test_f16_refused_by_name(lib):
+    for args, arg in [
+        ((A, moe.MOE_F16, 2, 2, 8, None, 1.0, None, moe.MOE_BF16, None, A2, moe.MOE_BF16), "expert_out"),
+        ((A, moe.MOE_BF16, 2, 2, 8, None, 1.0, A, moe.MOE_F16, None, A2, moe.MOE_BF16), "shared"),
+        ((A, moe.MOE_BF16, 2, 2, 8, None, 1.0, None, moe.MOE_BF16, None, A2, moe.MOE_F16), "out"),
+    ]:
+        st = lib.moe_combine_gate(*args, None)
+        assert st == 2
+        m = _err(lib)
+        assert "moe_combine_gate" in m and arg in m and "f16" in m
+
+
+def test_unknown_dtype_refused(lib):
+    st = lib.moe_combine_gate(A, 7, 2, 2, 8, None, 1.0, None, 1, None, A2, 1, None)
+    assert st == 2 and "unknown" in _err(lib)
+
+
+@pytest.mark.parametrize("T,E,K", [(4, 8, 0), (4, 8, 9), (4, 2000, 2), (4, 64, 33), (-1, 8, 2)])
+def test_route_shape_refusals(lib, T, E, K):
+    st = lib.moe_route(A, T, E, K, A, A, A, A, None, 0, None)
+    assert st == 3
+    assert "moe_route" in _err(lib)
+
+
+def test_route_null_outputs_refused(lib):
+    st = lib.moe_route(A, 4, 8, 2, None, A, A, A, None, 0, None)
+    assert st == 1 and "topk_ids" in _err(lib)
+    st = lib.moe_route(A, 4, 8, 2, A, A, None, A, None, 0, None)
+    assert st == 1 and "expert_offsets" in _err(lib)
+
+
+def test_gemm_refusals(lib):
+    f = lib.moe_grouped_gemm_gateup_silu
+    assert f(A, 4, 12, A, 8, 16, A, A, 2, A, None) == 3 and "H=12" in _err(lib)
+    assert f(A, 4, 16, A, 8, 12, A, A, 2, A, None) == 3 and "I=12" in _err(lib)
+    assert f(A, 4, 16, A, 8, 16, A, None, 2, A, None) == 1 and "both" in _err(lib)
+    assert f(A, 4, 16, A, 8, 16, None, None, 2, A, None) == 1 and "identity" in _err(lib)
+    assert f(MIS, 4, 16, A, 8, 16, A, A, 2, A, None) == 1 and "aligned" in _err(lib)
+    assert f(A, 4, 16, None, 8, 16, A, A, 2, A, None) == 1 and "w_gu" in _err(lib)
+    d = lib.moe_grouped_gemm_down
+    assert d(A, 8, 16, A, 8, 20, A, A, None, A, None) == 3 and "H=20" in _err(lib)
+    assert d(A, 8, 16, A, 8, 16, None, None, None, A, None) == 1 and "identity" in _err(lib)
+    assert d(A, 8, 16, A, 1, 16, None, None, None, MIS, None) == 1 and "expert_out" in _err(lib)
+    r = lib.moe_router_logits
+    assert r(A, 4, 10, A, 8, None, A, None) == 3
+    assert r(A, 4, 16, A, 0, None, A, None) == 3
+
+
+def test_combine_scale_and_gate_refusals(lib):
+    c = lib.moe_combine_gate
+    assert c(A, 1, 2, 2, 8, None, math.inf, None, 1, None, A2, 1, None) == 1
+    assert "routed_scale" in _err(lib)
+    assert c(A, 1, 2, 2, 8, None, math.nan, None, 1, None, A2, 1, None) == 1
+    assert c(A, 1, 2, 2, 8, None, 1.0, None, 1, A, A2, 1, None) == 1
+    assert "gate_logit" in _err(lib)
+    assert c(A, 1, 2, 0, 8, None, 1.0, None, 1, None, A2, 1, None) == 3
+    assert c(A, 1, 2, 2, 12, None, 1.0, None, 1, None, A2, 1, None) == 3
+    assert c(A, 1, 2, 2, 8, None, 1.0, MIS, 1, None, A2, 1, None) == 1
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    assert lib.moe_combine_gate(None, 1, 0, 2, 8, None, 1.0, None, 1, None, None, 1, None) == 0
+    assert lib.moe_route(None, 0, 8, 2, None, None, A, None, None, 0, None) == 0
+    assert lib.moe_grouped_gemm_gateup_silu(None, 0, 16, None, 8, 16, A, A, 2, None, None) == 0
+    assert lib.moe_grouped_gemm_down(None, 0, 16, None, 8, 16, A, A, None, None, None) == 0
+    assert lib.moe_router_logits(None, 0, 16, None, 8, None, None, None) == 0
+    assert _err(lib) == ""
+
+
+def test_route_workspace_query(lib):
+    assert lib.moe_route_workspace_bytes(8192, 128, 8) == 0
+
+
+def test_error_is_cleared_by_next_call(lib):
+    lib.moe_combine_gate(A, moe.MOE_F16, 2, 2, 8, None, 1.0, None, 1, None, A2, 1, None)
+    assert _err(lib) != ""
+    lib.moe_route_workspace_bytes(1, 1, 1)
+    lib.moe_combine_gate(None, 1, 0, 2, 8, None, 1.0, None, 1, None, None, 1, None)
+    assert _err(lib) == ""
+
+
+def test_valid_call_without_gpu_fails_at_device_check(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case is for hosts without one")
+    st = lib.moe_combine_gate(A, 1, 2, 2, 8, None, 1.0, None, 1, None, A2, 1, None)
+    assert st == 5 and "moe_combine_gate" in _err(lib)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        moe.load()
+
+
+def test_product_code_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "mixture_experts_ffn_expert_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, fn
+                assert "moe_oracle" not in txt, fn

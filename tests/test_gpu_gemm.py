@@ -1,0 +1,222 @@
+"""GPU parity of the grouped GEMMs and the logits helper.
+
+* Exact-arithmetic inputs (small integers times powers of two, every partial
+  sum exact in f32) make the GEMMs independent of summation order, so the GPU
+  must match the oracle bit for bit, through both kernel shapes (weight
+  streaming for few rows per expert, LDS tiles for many), ragged row counts,
+  empty experts and column / k tails; the hand-derived golden fixtures (N1,
+  N2, gather, scatter) run bit-exact too.
+* Random bf16 inputs at the workload shapes: stage-wise (the GPU stage gets
+  the oracle's routing) within 2 bf16 ulp / 1e-2 rms and NMSE <= 1e-5; the
+  8192-token skewed workload is checked on sampled rows, the launch
+  configuration being the one the benchmark times.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from conftest import cached_inputs
+from gpu_helpers import (DEV, assert_bits_equal, assert_gemm_close, bits, sample_rows, sub_down,
+                         sub_gateup, to_dev, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+
+
+def _exact_bf16(seed, shape, lo, hi, scale):
+    g = np.random.Generator(np.random.PCG64(seed))
+    v = (g.integers(lo, hi + 1, size=shape).astype(np.float64) * scale).astype(F32)
+    b = O.bf16_from_f32(v)
+    assert np.array_equal(O.f32_from_bf16(b), v)
+    return b
+
+
+def _routing_for(T, E, K, seed, skew=False):
+    g = np.random.Generator(np.random.PCG64(seed))
+    l = g.standard_normal((T, E)).astype(F32)
+    if skew:
+        l += (3.0 * np.log(1.0 / (1.0 + np.arange(E)))).astype(F32)
+    ids, w, off, sp = O.route(l, K)
+    return ids, w, off, sp
+
+
+# (T, H, E, K, I): avg rows/expert T*K/E spans the streaming (<= 8, <= 24) and
+# tiled kernels; H, I not multiples of the tile sizes to exercise tails.
+EXACT_SHAPES = [
+    (16, 64, 8, 2, 32),       # 4 rows/expert, tiny
+    (40, 136, 16, 3, 40),     # 7.5 rows/expert, k tail, column tail
+    (96, 256, 16, 4, 72),     # 24 rows/expert -> 32-row streaming tiles
+    (300, 328, 8, 2, 200),    # 75 rows/expert -> LDS tiles, ragged
+    (700, 512, 12, 3, 136),   # 175 rows/expert, several m tiles per expert
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,I", EXACT_SHAPES)
+@pytest.mark.parametrize("skew", [False, True])
+def test_gemms_bit_exact_on_exact_arithmetic(gpu_lib, T, H, E, K, I, skew):
+    print(f"exact gemm T={T} H={H} E={E} K={K} I={I} skew={skew}", flush=True)
+    seed = T * 7 + H + E * 3 + K + I + int(skew)
+    x = _exact_bf16(seed, (T, H), -4, 4, 1.0)
+    wgu = _exact_bf16(seed + 1, (E, 2 * I, H), -4, 4, 2.0 ** -6)
+    ids, w, off, sp = _routing_for(T, E, K, seed + 2, skew)
+    if skew:
+        assert np.any(np.diff(off) == 0), "expected empty experts"
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), to_dev_bf16(wgu), to_dev(sp),
+                                               to_dev(off), K)
+    torch.cuda.synchronize()
+    ref_act = O.gateup_silu(x, wgu, sp, off, K)
+    assert_bits_equal(bits(act), ref_act, "act")
+    # down on an exact act (its own values) so the sums stay exact
+    a2 = _exact_bf16(seed + 3, (T * K, I), -8, 8, 2.0 ** -4)
+    wd = _exact_bf16(seed + 4, (E, H, I), -4, 4, 2.0 ** -5)
+    eo = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), to_dev_bf16(wd), to_dev(sp), to_dev(off),
+                                       to_dev(w.reshape(-1)))
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(eo), O.down_proj(a2, wd, sp, off, w.reshape(-1)), "expert_out")
+    eo0 = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), to_dev_bf16(wd), to_dev(sp), to_dev(off),
+                                        None)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(eo0), O.down_proj(a2, wd, sp, off, None), "expert_out unweighted")
+
+
+@pytest.mark.parametrize("T,H,I", [(16, 64, 32), (512, 264, 72), (40, 128, 512)])
+def test_identity_rows_bit_exact(gpu_lib, T, H, I):
+    """NULL sorted_pairs/offsets: a dense expert (the shared expert)."""
+    x = _exact_bf16(T + H, (T, H), -4, 4, 1.0)
+    wgu = _exact_bf16(I + 1, (1, 2 * I, H), -4, 4, 2.0 ** -6)
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), to_dev_bf16(wgu), None, None, 1)
+    a2 = _exact_bf16(I + 2, (T, I), -8, 8, 2.0 ** -4)
+    wd = _exact_bf16(I + 3, (1, H, I), -4, 4, 2.0 ** -5)
+    sd = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), to_dev_bf16(wd), None, None, None)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(act), O.gateup_silu(x, wgu, None, None, 1), "shared act")
+    assert_bits_equal(bits(sd), O.down_proj(a2, wd, None, None, None), "shared down")
+
+
+def _golden():
+    return json.load(open(os.path.join(os.path.dirname(__file__), "golden", "gemm_cases.json")))
+
+
+def _pad(a, axis_sizes):
+    out = np.zeros(axis_sizes, np.float32)
+    out[tuple(slice(0, s) for s in np.shape(a))] = a
+    return out
+
+
+@pytest.mark.parametrize("case", _golden()["gateup"], ids=lambda c: c["name"])
+def test_gateup_golden_on_gpu(gpu_lib, case):
+    T, H, E, K, I = case["T"], case["H"], case["E"], case["K"], case["I"]
+    Hp, Ip = 8, 8                       # zero padding keeps every value
+    x = O.bf16_from_f32(_pad(np.array(case["x"], F32), (T, Hp)))
+    wg = np.array(case["w_gu"], F32)
+    wgu = np.zeros((E, 2 * Ip, Hp), F32)
+    wgu[:, :I, :H] = wg[:, :I]
+    wgu[:, Ip:Ip + I, :H] = wg[:, I:]
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), to_dev_bf16(O.bf16_from_f32(wgu)),
+                                               to_dev(np.array(case["sorted_pairs"], np.int32)),
+                                               to_dev(np.array(case["offsets"], np.int32)), K)
+    torch.cuda.synchronize()
+    got = O.f32_from_bf16(bits(act))[:, :I]
+    assert np.array_equal(got, np.array(case["expected_act"], F32))
+
+
+@pytest.mark.parametrize("case", _golden()["down"], ids=lambda c: c["name"])
+def test_down_golden_on_gpu(gpu_lib, case):
+    P, I, E, H = case["P"], case["I"], case["E"], case["H"]
+    Ip, Hp = 8, 8
+    act = O.bf16_from_f32(_pad(np.array(case["act"], F32), (P, Ip)))
+    wd = O.bf16_from_f32(_pad(np.array(case["w_d"], F32), (E, Hp, Ip)))
+    eo = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(act), to_dev_bf16(wd),
+                                       to_dev(np.array(case["sorted_pairs"], np.int32)),
+                                       to_dev(np.array(case["offsets"], np.int32)),
+                                       to_dev(np.array(case["pair_w"], F32)))
+    torch.cuda.synchronize()
+    got = O.f32_from_bf16(bits(eo))[:, :H]
+    assert np.array_equal(got, np.array(case["expected_out"], F32))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_gemms_stagewise_workloads(gpu_lib, n):
+    d = cached_inputs(n)
+    cfg = d["cfg"]
+    print(f"stagewise gemm cfg={n} T={cfg.T}", flush=True)
+    logits = O.router_logits(d["x"], d["w_r"], d.get("router_bias"))
+    ids, w, off, sp = O.route(logits, cfg.K)
+    x_d, wgu_d, wd_d = to_dev_bf16(d["x"]), to_dev_bf16(d["w_gu"]), to_dev_bf16(d["w_d"])
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(x_d, wgu_d, to_dev(sp), to_dev(off), cfg.K)
+    torch.cuda.synchronize()
+    ref_act = O.gateup_silu(d["x"], d["w_gu"], sp, off, cfg.K)
+    assert_gemm_close(bits(act), ref_act, f"cfg{n} act")
+    # down from the oracle's act
+    eo = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(ref_act), wd_d, to_dev(sp), to_dev(off),
+                                       to_dev(w.reshape(-1)))
+    torch.cuda.synchronize()
+    assert_gemm_close(bits(eo), O.down_proj(ref_act, d["w_d"], sp, off, w.reshape(-1)),
+                      f"cfg{n} expert_out")
+    if "w_gu_s" in d:
+        sa = gpu_lib.moe_grouped_gemm_gateup_silu(x_d, to_dev_bf16(d["w_gu_s"][None]), None, None, 1)
+        torch.cuda.synchronize()
+        ref_sa = O.gateup_silu(d["x"], d["w_gu_s"][None], None, None, 1)
+        assert_gemm_close(bits(sa), ref_sa, f"cfg{n} shared act")
+        sd = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(ref_sa), to_dev_bf16(d["w_d_s"][None]),
+                                           None, None, None)
+        torch.cuda.synchronize()
+        assert_gemm_close(bits(sd), O.down_proj(ref_sa, d["w_d_s"][None], None, None, None),
+                          f"cfg{n} shared out")
+
+
+def test_gemms_skewed_full_size_sampled(gpu_lib):
+    d = cached_inputs(5)
+    cfg = d["cfg"]
+    print(f"skewed full-size gemm T={cfg.T} H={cfg.H} I={cfg.I}", flush=True)
+    logits = O.router_logits(d["x"], d["w_r"], d["router_bias"])
+    ids, w, off, sp = O.route(logits, cfg.K)
+    assert np.count_nonzero(np.diff(off) == 0) > 0, "skewed routing leaves experts empty"
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(d["x"]), to_dev_bf16(d["w_gu"]),
+                                               to_dev(sp), to_dev(off), cfg.K)
+    eo = gpu_lib.moe_grouped_gemm_down(act, to_dev_bf16(d["w_d"]), to_dev(sp), to_dev(off),
+                                       to_dev(w.reshape(-1)))
+    torch.cuda.synchronize()
+    qs = sample_rows(off, 3, seed=5)
+    act_h = bits(act)
+    ref_act = sub_gateup(d["x"], d["w_gu"], sp, off, cfg.K, qs)
+    assert_gemm_close(act_h[qs], ref_act, "cfg5 act (sampled)")
+    ref_eo = sub_down(act_h[qs], d["w_d"], off, qs, w.reshape(-1)[sp[qs]])
+    assert_gemm_close(bits(eo)[sp[qs]], ref_eo, "cfg5 expert_out (sampled)")
+
+
+@pytest.mark.parametrize("T,H,N,bias", [(16, 64, 8, False), (32, 2048, 128, False),
+                                        (512, 2048, 1, False), (1000, 4096, 128, True),
+                                        (8192, 4096, 128, True)])
+def test_router_logits_within_f32_bound(gpu_lib, T, H, N, bias):
+    x = W.random_bf16(T + 1, (T, H))
+    w = W.random_bf16(N + 2, (N, H), 1.0 / np.sqrt(H))
+    b = W.random_f32(3, (N,)) if bias else None
+    out = gpu_lib.moe_router_logits(to_dev_bf16(x), to_dev_bf16(w), None if b is None else to_dev(b))
+    torch.cuda.synchronize()
+    ref = O.router_logits(x, w, b).astype(np.float64)
+    xf = O.f32_from_bf16(x).astype(np.float64)
+    wf = O.f32_from_bf16(w).astype(np.float64)
+    mag = np.abs(xf) @ np.abs(wf).T + (0 if b is None else np.abs(b)[None, :])
+    err = np.abs(bits(out).astype(np.float64) - ref)
+    # f32 accumulation: about H/16 rounded adds -> error well under 2^-14 of sum of abs terms
+    assert np.all(err <= 2.0 ** -14 * mag + 1e-30), float(np.max(err / (mag + 1e-30)))
+
+
+def test_gemm_output_canaries(gpu_lib):
+    T, H, E, K, I = 40, 136, 16, 3, 40
+    x = _exact_bf16(1, (T, H), -4, 4, 1.0)
+    wgu = _exact_bf16(2, (E, 2 * I, H), -4, 4, 2.0 ** -6)
+    ids, w, off, sp = _routing_for(T, E, K, 3)
+    full = torch.full((T * K * I + 256,), 0x7BCD, dtype=torch.int16, device=DEV)
+    act = full[: T * K * I].view(torch.bfloat16).view(T * K, I)
+    gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), to_dev_bf16(wgu), to_dev(sp), to_dev(off),
+                                         K, act=act)
+    torch.cuda.synchronize()
+    assert torch.all(full[T * K * I:] == 0x7BCD).item(), "gate-up wrote past act"
+    assert_bits_equal(bits(act), O.gateup_silu(x, wgu, sp, off, K), "act")
