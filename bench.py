@@ -76,6 +76,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; the expert-parallel multi-GPU "
@@ -91,6 +93,16 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = 1 << 29                               # 2^29 bf16 = 1 GiB read + 1 GiB written
+        a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
+                          "launches": 3}))
+        return
     moe.load()
     moe.moe_init()
     d = workloads.make_inputs(args.workload)

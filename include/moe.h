@@ -45,7 +45,8 @@
  *   - A call with zero tokens (T == 0 or P == 0) returns MOE_OK and does
  *     nothing.
  *   - Limits: 1 <= K <= E, E <= 1024, K <= 32, H and I multiples of 8,
- *     T*K < 2^31, T*max(H,I,E) < 2^31 elements per tensor row block.
+ *     T*K, T*E, T*K*I and T*K*H below 2^31 elements; the GEMM operands x,
+ *     act and one expert's weight block (2I*H, H*I) below 2^30 elements.
  */
 #ifndef MOE_H
 #define MOE_H

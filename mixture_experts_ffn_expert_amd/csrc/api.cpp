@@ -98,6 +98,10 @@ moe_status hip_status(const char* fn, hipError_t e) {
 
 bool fits_i32(long long v) { return v >= 0 && v < (1LL << 31); }
 
+// The GEMM kernels address each operand matrix (and each expert's weight
+// block) through a buffer resource of at most 2^31 bytes: 2^30 bf16 values.
+bool fits_buf(long long elems) { return elems >= 0 && elems < (1LL << 30); }
+
 }  // namespace
 
 extern "C" {
@@ -116,8 +120,8 @@ moe_status moe_router_logits(const uint16_t* x, int T, int H, const uint16_t* w,
   if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
   if (H <= 0 || H % 8) return fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);
   if (N < 1) return fail(MOE_E_SHAPE, "%s: N=%d must be >= 1", fn, N);
-  if (!fits_i32((long long)T * H) || !fits_i32((long long)T * N) || !fits_i32((long long)N * H))
-    return fail(MOE_E_SHAPE, "%s: T*H, T*N or N*H exceeds 2^31 elements", fn);
+  if (!fits_buf((long long)T * H) || !fits_i32((long long)T * N) || !fits_buf((long long)N * H))
+    return fail(MOE_E_SHAPE, "%s: T*H or N*H exceeds 2^30 elements, or T*N 2^31", fn);
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(fn, x);
   REQUIRE_PTR(fn, w);
@@ -180,9 +184,10 @@ moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const u
   if (sorted_pairs == nullptr && (E != 1 || K != 1))
     return fail(MOE_E_INVALID, "%s: identity rows (NULL sorted_pairs) need E=1 and K=1, got E=%d K=%d",
                 fn, E, K);
-  if (!fits_i32((long long)T * K) || !fits_i32((long long)T * H) ||
-      !fits_i32((long long)T * K * I) || !fits_i32(2LL * I * H))
-    return fail(MOE_E_SHAPE, "%s: a tensor exceeds 2^31 elements per expert/row block", fn);
+  if (!fits_i32((long long)T * K) || !fits_buf((long long)T * H) ||
+      !fits_i32((long long)T * K * I) || !fits_buf(2LL * I * H))
+    return fail(MOE_E_SHAPE, "%s: x or one expert's w_gu exceeds 2^30 elements, or T*K*I 2^31",
+                fn);
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(fn, x);
   REQUIRE_PTR(fn, w_gu);
@@ -208,8 +213,8 @@ moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const uint16
                 fn);
   if (sorted_pairs == nullptr && E != 1)
     return fail(MOE_E_INVALID, "%s: identity rows (NULL sorted_pairs) need E=1, got E=%d", fn, E);
-  if (!fits_i32((long long)P * I) || !fits_i32((long long)P * H) || !fits_i32((long long)H * I))
-    return fail(MOE_E_SHAPE, "%s: a tensor exceeds 2^31 elements per expert/row block", fn);
+  if (!fits_buf((long long)P * I) || !fits_i32((long long)P * H) || !fits_buf((long long)H * I))
+    return fail(MOE_E_SHAPE, "%s: act or one expert's w_d exceeds 2^30 elements, or P*H 2^31", fn);
   if (P == 0) return MOE_OK;
   REQUIRE_PTR(fn, act);
   REQUIRE_PTR(fn, w_d);

@@ -21,12 +21,13 @@
 // once.
 //
 // Two kernel shapes:
-//  * stream_kernel (few rows per expert, e.g. decode): one wave owns a 16- or
-//    32-row block and a slab of output columns over the whole k range. Each
-//    weight element is used by exactly one wave, so weights go straight from
-//    HBM into MFMA operand registers (v_mfma_f32_16x16x32_bf16) with no LDS
-//    and no barrier in the k loop; the k loop is unrolled so each wave keeps
-//    several KiB of loads in flight. HBM-bound by design.
+//  * stream_kernel (few rows per expert, e.g. decode): a workgroup owns a 16-
+//    or 32-row block of one expert and 16 or 32 output columns; its 4 waves
+//    split the k range. Each weight element is used by exactly one wave, so
+//    weights go straight from HBM into MFMA operand registers
+//    (v_mfma_f32_16x16x32_bf16) with no LDS staging and no barrier in the k
+//    loop; the partial tiles meet once in LDS, added in a fixed order. The
+//    small work units keep every CU streaming to the end. HBM-bound by design.
 //  * tiled_kernel (hundreds of rows per expert, prefill): 128 x 128 block
 //    tile, 4 waves of 64 x 64, k step 64 staged through LDS with padded rows
 //    (conflict-free 16-byte reads), register prefetch of the next k step
@@ -109,35 +110,6 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& g, int BM, int slot, i
   return false;
 }
 
-// Pointer to the A row of problem row q (null: zero row).
-__device__ __forceinline__ const uint16_t* a_row_ptr(const GemmArgs& g, int q) {
-  int r = q;
-  if (g.sorted != nullptr && g.gather_k > 0) {
-    const int p = g.sorted[q];
-    if (p < 0) return nullptr;
-    r = p / g.gather_k;
-  }
-  if (r < 0 || r >= g.a_rows) return nullptr;
-  return g.A + (size_t)r * g.kdim;
-}
-
-// B row of output column c for fragment kind (0: gate/plain, 1: up).
-template <int EPI>
-__device__ __forceinline__ const uint16_t* b_row_ptr(const GemmArgs& g, int e, int c, int up) {
-  if (c >= g.n_out) return nullptr;
-  const int r = (EPI == EPI_GATEUP && up) ? g.n_out + c : c;
-  return g.B + ((size_t)e * g.b_rows + r) * g.kdim;
-}
-
-__device__ __forceinline__ bf16x8_t load8(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8_t*>(p);
-}
-
-__device__ __forceinline__ bf16x8_t zero8() {
-  u32x4_t z = {0u, 0u, 0u, 0u};
-  return __builtin_bit_cast(bf16x8_t, z);
-}
-
 // Epilogue of one output element (row q of the problem, column c).
 template <int EPI>
 __device__ __forceinline__ void store_plain(const GemmArgs& g, int q, int c, float acc) {
@@ -165,37 +137,82 @@ __device__ __forceinline__ void store_gateup(const GemmArgs& g, int q, int c, fl
 }
 
 // ---------------------------------------------------------------------------
-// stream_kernel: MF 16-row fragments x NFO 16-column output fragments per wave
+// Buffer loads. A raw buffer load whose byte offset lies past the resource's
+// size returns zero without touching memory, so rows past the end of a tile,
+// columns past n_out and k past kdim are read as zeros with no branch: every
+// lane keeps one fixed byte offset (kOob for a zero row) and the k position
+// goes into the scalar offset. Buffer sizes stay below 2^31 bytes (checked
+// at the C ABI), so kOob plus any k offset stays out of range.
 // ---------------------------------------------------------------------------
-template <int EPI, int MF, int NFO>
-__global__ __launch_bounds__(256) void stream_kernel(GemmArgs g) {
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ bf16x8_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Byte offset of the A row of problem row q inside A (kOob: zero row).
+__device__ __forceinline__ uint32_t a_row_off(const GemmArgs& g, int q) {
+  int r = q;
+  if (g.sorted != nullptr && g.gather_k > 0) {
+    const int p = g.sorted[q];
+    if (p < 0) return kOob;
+    r = p / g.gather_k;
+  }
+  if (r < 0 || r >= g.a_rows) return kOob;
+  return (uint32_t)r * (uint32_t)g.kdim * 2u;
+}
+
+// Byte offset of the weight row of output column c inside expert e's block.
+template <int EPI>
+__device__ __forceinline__ uint32_t b_row_off(const GemmArgs& g, int c, int up) {
+  if (c >= g.n_out) return kOob;
+  const int r = (EPI == EPI_GATEUP && up) ? g.n_out + c : c;
+  return (uint32_t)r * (uint32_t)g.kdim * 2u;
+}
+
+// ---------------------------------------------------------------------------
+// stream_kernel: one workgroup = 16*MF rows x 16*NFO output columns; its KS
+// waves split the k range into contiguous parts and add their partial tiles
+// in LDS in a fixed wave order (deterministic). Splitting k makes the work
+// units small enough to balance HBM streaming across all CUs.
+// ---------------------------------------------------------------------------
+template <int EPI, int MF, int NFO, int KS, int U>
+__global__ __launch_bounds__(64 * KS) void stream_kernel(GemmArgs g) {
   constexpr int NB = (EPI == EPI_GATEUP) ? 2 * NFO : NFO;  // B fragments per wave
   constexpr int BM = 16 * MF;
-  constexpr int COLS_PER_WAVE = 16 * NFO;
+  __shared__ float red[KS][MF][NB][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int blk = blockIdx.x;
   const int slot = blk / g.nblk;
   const int nb = blk - slot * g.nblk;
   int e, row0, rows;
-  if (!find_tile(g, BM, slot, e, row0, rows)) return;
-  const int col0 = (nb * 4 + wave) * COLS_PER_WAVE;
-  if (col0 >= g.n_out) return;
+  if (!find_tile(g, BM, slot, e, row0, rows)) return;  // uniform over the workgroup
+  const int col0 = nb * 16 * NFO;
 
   const int r16 = lane & 15;
   const int kc = (lane >> 4) * 8;
-  const uint16_t* pa[MF];
+  const __amdgpu_buffer_rsrc_t ra_rsrc =
+      make_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
+  const __amdgpu_buffer_rsrc_t rb_rsrc =
+      make_rsrc(g.B + (size_t)e * g.b_rows * g.kdim, (uint32_t)g.b_rows * (uint32_t)g.kdim * 2u);
+  uint32_t va[MF];
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
     const int rr = i * 16 + r16;
-    pa[i] = (rr < rows) ? a_row_ptr(g, row0 + rr) : nullptr;
+    va[i] = ((rr < rows) ? a_row_off(g, row0 + rr) : kOob) + kc * 2;
   }
-  const uint16_t* pb[NB];
+  uint32_t vb[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f) {
     const int fo = (EPI == EPI_GATEUP) ? (f >> 1) : f;
     const int up = (EPI == EPI_GATEUP) ? (f & 1) : 0;
-    pb[f] = b_row_ptr<EPI>(g, e, col0 + fo * 16 + r16, up);
+    vb[f] = b_row_off<EPI>(g, col0 + fo * 16 + r16, up) + kc * 2;
   }
   f32x4_t acc[MF][NB];
 #pragma unroll
@@ -203,19 +220,21 @@ __global__ __launch_bounds__(256) void stream_kernel(GemmArgs g) {
 #pragma unroll
     for (int f = 0; f < NB; ++f) acc[i][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int U = 4;  // k steps of 32 per unrolled iteration
-  const int kmain = (g.kdim / (32 * U)) * (32 * U);
-  int k0 = 0;
-  for (; k0 < kmain; k0 += 32 * U) {
+  // this wave's k range: a multiple of 32 elements (the last one may be short)
+  const int ksteps = (g.kdim + 31) >> 5;
+  const int kper = ((ksteps + KS - 1) / KS) * 32;
+  const int kb = min(g.kdim, __builtin_amdgcn_readfirstlane(wave) * kper);
+  const int ke = min(g.kdim, kb + kper);
+  int k0 = kb;
+  for (; k0 + 32 * U <= ke; k0 += 32 * U) {
     bf16x8_t a[U][MF], b[U][NB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const uint32_t soff = (uint32_t)(k0 + u * 32) * 2u;
 #pragma unroll
-      for (int f = 0; f < NB; ++f)
-        b[u][f] = pb[f] ? load8(pb[f] + k0 + u * 32 + kc) : zero8();
+      for (int f = 0; f < NB; ++f) b[u][f] = bload8(rb_rsrc, vb[f], soff);
 #pragma unroll
-      for (int i = 0; i < MF; ++i)
-        a[u][i] = pa[i] ? load8(pa[i] + k0 + u * 32 + kc) : zero8();
+      for (int i = 0; i < MF; ++i) a[u][i] = bload8(ra_rsrc, va[i], soff);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -225,13 +244,14 @@ __global__ __launch_bounds__(256) void stream_kernel(GemmArgs g) {
         for (int f = 0; f < NB; ++f)
           acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][f], acc[i][f], 0, 0, 0);
   }
-  for (; k0 < g.kdim; k0 += 32) {  // tail: 8-element chunks past kdim read as zero
-    const bool in = k0 + kc < g.kdim;
+  for (; k0 < ke; k0 += 32) {  // tail: 8-element chunks at or past ke read as zero
+    const bool in = k0 + kc < ke;
+    const uint32_t soff = (uint32_t)k0 * 2u;
     bf16x8_t a[MF], b[NB];
 #pragma unroll
-    for (int f = 0; f < NB; ++f) b[f] = (in && pb[f]) ? load8(pb[f] + k0 + kc) : zero8();
+    for (int f = 0; f < NB; ++f) b[f] = bload8(rb_rsrc, in ? vb[f] : kOob, soff);
 #pragma unroll
-    for (int i = 0; i < MF; ++i) a[i] = (in && pa[i]) ? load8(pa[i] + k0 + kc) : zero8();
+    for (int i = 0; i < MF; ++i) a[i] = bload8(ra_rsrc, in ? va[i] : kOob, soff);
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -239,12 +259,28 @@ __global__ __launch_bounds__(256) void stream_kernel(GemmArgs g) {
         acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
   }
 
-  // C layout of 16x16: element r of lane l is row (l/16)*4 + r, column l%16
 #pragma unroll
-  for (int i = 0; i < MF; ++i) {
+  for (int i = 0; i < MF; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int f = 0; f < NB; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][i][f][r][lane] = acc[i][f][r];
+  __syncthreads();
+
+  // C layout of 16x16: element r of lane l is row (l/16)*4 + r, column l%16.
+  // Wave w finishes the elements r = w, w + KS, ...: sum over waves 0..KS-1.
+  for (int r = wave; r < 4; r += KS) {
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
       const int rr = i * 16 + (lane >> 4) * 4 + r;
+      float sum[NB];
+#pragma unroll
+      for (int f = 0; f < NB; ++f) {
+        float s = red[0][i][f][r][lane];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) s = s + red[w][i][f][r][lane];  // fixed order
+        sum[f] = s;
+      }
       if (rr >= rows) continue;
       const int q = row0 + rr;
 #pragma unroll
@@ -252,34 +288,43 @@ __global__ __launch_bounds__(256) void stream_kernel(GemmArgs g) {
         const int c = col0 + fo * 16 + r16;
         if (c >= g.n_out) continue;
         if (EPI == EPI_GATEUP)
-          store_gateup(g, q, c, acc[i][2 * fo][r], acc[i][2 * fo + 1][r]);
+          store_gateup(g, q, c, sum[2 * fo], sum[2 * fo + 1]);
         else
-          store_plain<EPI>(g, q, c, acc[i][fo][r]);
+          store_plain<EPI>(g, q, c, sum[fo]);
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// tiled_kernel: 128 x 128 tile, 4 waves (2 x 2) of 64 x 64, k step 64 in LDS
+// tiled_kernel: BM x BN block tile (BN weight rows), WM x WN waves, k step BK
+// staged through LDS with padded rows (BK = 64: 144-byte rows, conflict-free
+// 16-byte fragment reads). The next k step is loaded into registers while
+// the current one is multiplied (v_mfma_f32_32x32x16_bf16).
 // ---------------------------------------------------------------------------
-constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;
-
-template <int EPI>
-__global__ __launch_bounds__(256) void tiled_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[TBM * TLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[TBN * TLD];
+template <int EPI, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(GemmArgs g) {
+  constexpr int NT = 64 * WM * WN;             // threads
+  constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
+  constexpr int FM = TM / 32, FN = TN / 32;    // 32x32 fragments per wave
+  constexpr int LD = BK + 8;                   // padded LDS row (elements)
+  constexpr int CPR = BK / 8;                  // 16-byte chunks per row
+  constexpr int A_CH = BM * CPR / NT;          // chunks per thread
+  constexpr int B_CH = BN * CPR / NT;
+  constexpr int OUT_COLS = (EPI == EPI_GATEUP) ? BN / 2 : BN;
+  static_assert(A_CH * NT == BM * CPR && B_CH * NT == BN * CPR, "tile / thread mismatch");
+  static_assert(EPI != EPI_GATEUP || FN % 2 == 0, "gate-up pairs fragments");
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LD];
   __shared__ int tile_info[3];
-  constexpr int OUT_COLS = (EPI == EPI_GATEUP) ? TBN / 2 : TBN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int blk = blockIdx.x;
-  const int slot = blk / g.nblk;
-  const int nb = blk - slot * g.nblk;
+  const int slot = blockIdx.x / g.nblk;
+  const int nb = blockIdx.x - slot * g.nblk;
   if (wave == 0) {
     int e = 0, row0 = 0, rows = 0;
-    if (!find_tile(g, TBM, slot, e, row0, rows)) rows = 0;
+    if (!find_tile(g, BM, slot, e, row0, rows)) rows = 0;
     if (lane == 0) {
       tile_info[0] = e;
       tile_info[1] = row0;
@@ -291,93 +336,118 @@ __global__ __launch_bounds__(256) void tiled_kernel(GemmArgs g) {
   if (rows <= 0) return;
   const int n0 = nb * OUT_COLS;
 
-  // global -> LDS assignment: 8 threads per 64-element row, 32 rows per pass
-  const int lc = (tid & 7) * 8;
-  const uint16_t* ga[4];
-  const uint16_t* gb[4];
+  const __amdgpu_buffer_rsrc_t ra_rsrc =
+      make_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
+  const __amdgpu_buffer_rsrc_t rb_rsrc =
+      make_rsrc(g.B + (size_t)e * g.b_rows * g.kdim, (uint32_t)g.b_rows * (uint32_t)g.kdim * 2u);
+  uint32_t va[A_CH], vb[B_CH];  // per-thread byte offsets (k = 0)
+  int sa[A_CH], sb[B_CH];       // LDS element offsets
+  int ca[A_CH], cb[B_CH];       // k offset (elements) of the chunk within the step
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    ga[i] = (r < rows) ? a_row_ptr(g, row0 + r) : nullptr;
-    int c, up = 0;
+  for (int i = 0; i < A_CH; ++i) {
+    const int ci = tid + NT * i, r = ci / CPR, c = ci % CPR;
+    const uint32_t ro = (r < rows) ? a_row_off(g, row0 + r) : kOob;
+    va[i] = ro + c * 16;
+    sa[i] = r * LD + c * 8;
+    ca[i] = c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int ci = tid + NT * i, r = ci / CPR, c = ci % CPR;
+    int col, up = 0;
     if (EPI == EPI_GATEUP) {
-      const int wn = r >> 6, f = (r >> 5) & 1, j = r & 31;
-      c = n0 + wn * 32 + j;
-      up = f;
+      // wave column wn owns TN weight rows: fragment pairs (gate, up) of
+      // 32 output columns each
+      const int wn = r / TN, f = (r % TN) >> 5, j = r & 31;
+      col = n0 + wn * (TN / 2) + (f >> 1) * 32 + j;
+      up = f & 1;
     } else {
-      c = n0 + r;
+      col = n0 + r;
     }
-    gb[i] = b_row_ptr<EPI>(g, e, c, up);
+    vb[i] = b_row_off<EPI>(g, col, up) + c * 16;
+    sb[i] = r * LD + c * 8;
+    cb[i] = c * 8;
   }
 
-  const int wm = wave & 1, wn = wave >> 1;
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
-
-  bf16x8_t ra[4], rb[4];
+  bf16x8_t ra[A_CH], rb[B_CH];
   auto gload = [&](int k0) {
+    const uint32_t soff = (uint32_t)k0 * 2u;
+    if (k0 + BK <= g.kdim) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool in = k0 + lc < g.kdim;
-      ra[i] = (in && ga[i]) ? load8(ga[i] + k0 + lc) : zero8();
-      rb[i] = (in && gb[i]) ? load8(gb[i] + k0 + lc) : zero8();
+      for (int i = 0; i < A_CH; ++i) ra[i] = bload8(ra_rsrc, va[i], soff);
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) rb[i] = bload8(rb_rsrc, vb[i], soff);
+    } else {  // last, partial k step: chunks at or past kdim read as zero
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i)
+        ra[i] = bload8(ra_rsrc, (k0 + ca[i] < g.kdim) ? va[i] : kOob, soff);
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i)
+        rb[i] = bload8(rb_rsrc, (k0 + cb[i] < g.kdim) ? vb[i] : kOob, soff);
     }
   };
   auto sstore = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<bf16x8_t*>(&As[r * TLD + lc]) = ra[i];
-      *reinterpret_cast<bf16x8_t*>(&Bs[r * TLD + lc]) = rb[i];
-    }
+    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<bf16x8_t*>(&As[sa[i]]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) *reinterpret_cast<bf16x8_t*>(&Bs[sb[i]]) = rb[i];
   };
 
-  const int nk = (g.kdim + TBK - 1) / TBK;
-  gload(0);
+  const int wm = wave % WM, wn = wave / WM;
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+
+  const int nk = (g.kdim + BK - 1) / BK;
   const int r32 = lane & 31;
   const int kh = (lane >> 5) * 8;
+  const uint16_t* a_base = &As[(wm * TM + r32) * LD + kh];
+  const uint16_t* b_base = &Bs[(wn * TN + r32) * LD + kh];
+  gload(0);
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();
     sstore();
     __syncthreads();
-    if (kt + 1 < nk) gload((kt + 1) * TBK);
+    if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
-    for (int kk = 0; kk < TBK / 16; ++kk) {
-      bf16x8_t a[2], b[2];
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8_t a[FM], b[FN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(&As[(wm * 64 + i * 32 + r32) * TLD + kk * 16 + kh]);
+      for (int i = 0; i < FM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(a_base + i * 32 * LD + kk * 16);
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-        b[f] = *reinterpret_cast<const bf16x8_t*>(&Bs[(wn * 64 + f * 32 + r32) * TLD + kk * 16 + kh]);
+      for (int f = 0; f < FN; ++f)
+        b[f] = *reinterpret_cast<const bf16x8_t*>(b_base + f * 32 * LD + kk * 16);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < FN; ++f)
           acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
     }
   }
 
   // C layout of 32x32: element r of lane l is row (r/4)*8 + (l/32)*4 + r%4, column l%32
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rr = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const int rr = wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
       if (rr >= rows) continue;
       const int q = row0 + rr;
       if (EPI == EPI_GATEUP) {
-        const int c = n0 + wn * 32 + r32;
-        if (c < g.n_out) store_gateup(g, q, c, acc[i][0][r], acc[i][1][r]);
+#pragma unroll
+        for (int pp = 0; pp < FN / 2; ++pp) {
+          const int c = n0 + wn * (TN / 2) + pp * 32 + r32;
+          if (c < g.n_out) store_gateup(g, q, c, acc[i][2 * pp][r], acc[i][2 * pp + 1][r]);
+        }
       } else {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int c = n0 + wn * 64 + f * 32 + r32;
+        for (int f = 0; f < FN; ++f) {
+          const int c = n0 + wn * TN + f * 32 + r32;
           if (c < g.n_out) store_plain<EPI>(g, q, c, acc[i][f][r]);
         }
       }
@@ -393,29 +463,58 @@ static inline int slots_for(int P, int E, int BM, bool grouped) {
   return grouped ? full + (E < P ? E : P) : full;
 }
 
+// Grid of slots x nblk workgroups. Consecutive workgroups take adjacent
+// column blocks of one expert, i.e. adjacent weight rows: the chip streams
+// one contiguous region at a time, which measured faster than pinning an
+// expert's blocks to one XCD.
+static inline unsigned grid_for(const GemmArgs& g) {
+  return (unsigned)((long long)g.slots * g.nblk);
+}
+
 template <int EPI>
 static hipError_t dispatch(GemmArgs g, hipStream_t s) {
   const bool grouped = g.offsets != nullptr;
+  if constexpr (EPI == EPI_F32) {
+    // logits: few columns, long k; 16 waves split k so one round of loads
+    // covers k = 2048, every workgroup owns 16 rows x 32 columns
+    g.nblk = (g.n_out + 31) / 32;
+    g.slots = slots_for(g.P, g.E, 16, false);
+    hipLaunchKernelGGL((stream_kernel<EPI, 1, 2, 16, 4>), dim3(grid_for(g)), dim3(1024), 0,
+                       s, g);
+    return hipGetLastError();
+  } else {
   const double avg_rows = grouped ? (double)g.P / (double)g.E : (double)g.P;
   if (avg_rows <= 24.0) {
-    // few rows per expert: weight streaming, one wave per 16 (or 32) rows x 32 columns
-    constexpr int NFO = (EPI == EPI_GATEUP) ? 1 : 2;
-    const int cols_per_block = 4 * 16 * NFO;
-    g.nblk = (g.n_out + cols_per_block - 1) / cols_per_block;
+    // few rows per expert: weight streaming. Shapes measured at the decode
+    // and 256-expert workloads: gate-up 16 output columns (gate + up
+    // fragments) with k split 4 ways; down 16 columns, k split 2 ways (its k
+    // is the short intermediate size) for 16-row tiles, 32 columns split 4
+    // ways for 32-row tiles.
     if (avg_rows <= 8.0) {
       g.slots = slots_for(g.P, g.E, 16, grouped);
-      hipLaunchKernelGGL((stream_kernel<EPI, 1, NFO>), dim3(g.slots * g.nblk), dim3(256), 0, s, g);
+      g.nblk = (g.n_out + 15) / 16;
+      if constexpr (EPI == EPI_GATEUP)
+        hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 4, 4>), dim3(grid_for(g)), dim3(256), 0, s, g);
+      else
+        hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 2, 4>), dim3(grid_for(g)), dim3(128), 0, s, g);
     } else {
       g.slots = slots_for(g.P, g.E, 32, grouped);
-      hipLaunchKernelGGL((stream_kernel<EPI, 2, NFO>), dim3(g.slots * g.nblk), dim3(256), 0, s, g);
+      if constexpr (EPI == EPI_GATEUP) {
+        g.nblk = (g.n_out + 15) / 16;
+        hipLaunchKernelGGL((stream_kernel<EPI, 2, 1, 4, 4>), dim3(grid_for(g)), dim3(256), 0, s, g);
+      } else {
+        g.nblk = (g.n_out + 31) / 32;
+        hipLaunchKernelGGL((stream_kernel<EPI, 2, 2, 4, 2>), dim3(grid_for(g)), dim3(256), 0, s, g);
+      }
     }
   } else {
-    const int out_cols = (EPI == EPI_GATEUP) ? TBN / 2 : TBN;
-    g.nblk = (g.n_out + out_cols - 1) / out_cols;
-    g.slots = slots_for(g.P, g.E, TBM, grouped);
-    hipLaunchKernelGGL((tiled_kernel<EPI>), dim3(g.slots * g.nblk), dim3(256), 0, s, g);
+    constexpr int BM = 128, BN = 128;
+    g.nblk = (g.n_out + (EPI == EPI_GATEUP ? BN / 2 : BN) - 1) / (EPI == EPI_GATEUP ? BN / 2 : BN);
+    g.slots = slots_for(g.P, g.E, BM, grouped);
+    hipLaunchKernelGGL((tiled_kernel<EPI, BM, BN, 64, 2, 2>), dim3(grid_for(g)), dim3(256), 0, s, g);
   }
   return hipGetLastError();
+  }
 }
 
 hipError_t launch_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w_gu, int E, int I,

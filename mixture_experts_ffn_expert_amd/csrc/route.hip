@@ -7,9 +7,11 @@
 // ids).
 //
 // Kernel 1 (topk_kernel): one wavefront per token. Lane l holds logits
-//   e = l + 64*j. K rounds of a wavefront arg-max over (value desc, id asc)
-//   pick the experts; lane k keeps the k-th value, computes e_k = exp(l_k -
-//   l_0), every lane forms the same sequential f32 sum, lane k divides.
+//   e = l + 64*j as order-preserving integer keys. Each of the K rounds takes
+//   the wavefront maximum key (DPP reduction) and, by one ballot per j, the
+//   lowest expert id holding it, so ties go to the lower id; lane k keeps the
+//   k-th logit, computes e_k = exp(l_k - l_0), every lane forms the same
+//   sequential f32 sum, lane k divides.
 // Kernel 2 (group_kernel): one workgroup of 8 waves. Wave w owns a
 //   contiguous segment of pairs. (i) per-wave expert histogram in LDS,
 //   (ii) exclusive scan over experts of the totals and per-wave bases,
@@ -24,9 +26,19 @@ namespace moe {
 constexpr int kMaxE = 1024;
 constexpr int kMaxPerLane = kMaxE / 64;
 
-// a better than b: larger value, then lower id.
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+// Wavefront max of a 32-bit value (ROCm device library, DPP based).
+extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
+
+// Order-preserving map of a non-NaN float to uint32 (larger float, larger
+// key). +0 and -0 must be made equal by the caller. Every key is >= 1, so 0
+// marks "already taken".
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float lane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
@@ -37,60 +49,58 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;  // whole wave leaves together
   const float* row = logits + (size_t)t * E;
   const int nper = (E + 63) >> 6;
-  float v[kMaxPerLane];
+  uint32_t key[kMaxPerLane];
 #pragma unroll
   for (int j = 0; j < kMaxPerLane; ++j) {
-    int e = lane + 64 * j;
-    float x = -__builtin_inff();
+    const int e = lane + 64 * j;
+    uint32_t kj = 0;
     if (j < nper && e < E) {
-      x = row[e];
+      float x = row[e];
       if (x != x) x = -__builtin_inff();  // NaN ranks as -inf
+      if (x == 0.0f) x = 0.0f;            // -0 ties with +0
+      kj = order_key(x);
     }
-    v[j] = x;
+    key[j] = kj;
   }
-  uint32_t taken = 0;
-  float my_val = 0.0f;  // lane k keeps the k-th selected value
+  float my_val = 0.0f;  // lane k keeps the k-th selected logit
   int my_id = 0;
-  float top = 0.0f;
   for (int k = 0; k < K; ++k) {
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;  // sentinel: loses every tie against a real id
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) m = max(m, key[j]);
+    const uint32_t M = __ockl_wfred_max_u32(m);
+    // the lowest expert id holding the maximum: lower j first, then lower lane
+    int sel = 0;
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
-      int e = lane + 64 * j;
-      if (j < nper && e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) {
-        bv = v[j];
-        bi = e;
+      if (j >= nper) break;
+      const uint64_t hit = __ballot(key[j] == M);
+      if (hit) {
+        sel = (__ffsll((long long)hit) - 1) + 64 * j;
+        break;
       }
     }
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      float ov = __shfl_xor(bv, m);
-      int oi = __shfl_xor(bi, m);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    // the owner lane marks the winner as taken
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (k == 0) top = bv;
+    for (int j = 0; j < kMaxPerLane; ++j)
+      if (sel == lane + 64 * j) key[j] = 0;  // taken
     if (lane == k) {
-      my_val = bv;
-      my_id = bi;
+      float x = row[sel];
+      my_val = (x != x) ? -__builtin_inff() : x;
+      my_id = sel;
     }
   }
   // renormalised weights: e_k = exp(l_k - l_0), S = ((e_0 + e_1) + ...), w_k = e_k / S
-  float ek = 0.0f;
+  const float top = lane_f32(my_val, 0);
+  float ek;
   {
 #pragma clang fp contract(off)
-    float d = my_val - top;
+    const float d = my_val - top;
     ek = exp_cw(d);
   }
-  float S = __shfl(ek, 0);
+  float S = lane_f32(ek, 0);
   for (int k = 1; k < K; ++k) {
 #pragma clang fp contract(off)
-    S = S + __shfl(ek, k);
+    S = S + lane_f32(ek, k);
   }
   if (lane < K) {
     ids[(size_t)t * K + lane] = my_id;
