@@ -302,7 +302,7 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(GemmArgs g) {
 // 16-byte fragment reads). The next k step is loaded into registers while
 // the current one is multiplied (v_mfma_f32_32x32x16_bf16).
 // ---------------------------------------------------------------------------
-template <int EPI, int BM, int BN, int BK, int WM, int WN>
+template <int EPI, int BM, int BN, int BK, int WM, int WN, int PF = 1>
 __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(GemmArgs g) {
   constexpr int NT = 64 * WM * WN;             // threads
   constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
@@ -314,8 +314,18 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(GemmArgs g) {
   constexpr int OUT_COLS = (EPI == EPI_GATEUP) ? BN / 2 : BN;
   static_assert(A_CH * NT == BM * CPR && B_CH * NT == BN * CPR, "tile / thread mismatch");
   static_assert(EPI != EPI_GATEUP || FN % 2 == 0, "gate-up pairs fragments");
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LD];
+  static_assert(EPI != EPI_F32, "logits use the streaming kernel");
+  // Output staging: the bf16 result tile goes through LDS (reusing the
+  // operand buffers) in NP passes of BM/NP rows, then leaves as 16-byte row
+  // segments.
+  constexpr int CLD = OUT_COLS + 8;                              // padded row (elements)
+  constexpr int NP = (BM * CLD > (BM + BN) * LD) ? 2 : 1;
+  static_assert(BM % (NP * 32 * 1) == 0 && (BM / NP) * CLD <= (BM + BN) * LD, "staging");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[(BM + BN) * LD];
+  uint16_t* As = smem;
+  uint16_t* Bs = smem + BM * LD;
+  __shared__ int row_dest[BM];      // output row of each tile row (-1: none)
+  __shared__ float row_w[BM];       // routing weight of each tile row (down)
   __shared__ int tile_info[3];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -335,6 +345,21 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(GemmArgs g) {
   const int e = tile_info[0], row0 = tile_info[1], rows = tile_info[2];
   if (rows <= 0) return;
   const int n0 = nb * OUT_COLS;
+  for (int rr = tid; rr < BM; rr += NT) {
+    int dest = -1;
+    float wgt = 1.0f;
+    if (rr < rows) {
+      const int q = row0 + rr;
+      dest = q;
+      if (EPI == EPI_DOWN && g.sorted != nullptr) {
+        dest = g.sorted[q];
+        if (dest < 0 || dest >= g.P) dest = -1;
+      }
+      if (EPI == EPI_DOWN && g.pair_w != nullptr && dest >= 0) wgt = g.pair_w[dest];
+    }
+    row_dest[rr] = dest;
+    row_w[rr] = wgt;
+  }
 
   const __amdgpu_buffer_rsrc_t ra_rsrc =
       make_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
@@ -369,28 +394,30 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(GemmArgs g) {
     cb[i] = c * 8;
   }
 
-  bf16x8_t ra[A_CH], rb[B_CH];
-  auto gload = [&](int k0) {
+  // PF register stages: the loads of k step t + PF are issued while step t
+  // is multiplied
+  bf16x8_t ra[PF][A_CH], rb[PF][B_CH];
+  auto gload = [&](int st, int k0) {
     const uint32_t soff = (uint32_t)k0 * 2u;
     if (k0 + BK <= g.kdim) {
 #pragma unroll
-      for (int i = 0; i < A_CH; ++i) ra[i] = bload8(ra_rsrc, va[i], soff);
+      for (int i = 0; i < A_CH; ++i) ra[st][i] = bload8(ra_rsrc, va[i], soff);
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) rb[i] = bload8(rb_rsrc, vb[i], soff);
+      for (int i = 0; i < B_CH; ++i) rb[st][i] = bload8(rb_rsrc, vb[i], soff);
     } else {  // last, partial k step: chunks at or past kdim read as zero
 #pragma unroll
       for (int i = 0; i < A_CH; ++i)
-        ra[i] = bload8(ra_rsrc, (k0 + ca[i] < g.kdim) ? va[i] : kOob, soff);
+        ra[st][i] = bload8(ra_rsrc, (k0 + ca[i] < g.kdim) ? va[i] : kOob, soff);
 #pragma unroll
       for (int i = 0; i < B_CH; ++i)
-        rb[i] = bload8(rb_rsrc, (k0 + cb[i] < g.kdim) ? vb[i] : kOob, soff);
+        rb[st][i] = bload8(rb_rsrc, (k0 + cb[i] < g.kdim) ? vb[i] : kOob, soff);
     }
   };
-  auto sstore = [&]() {
+  auto sstore = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<bf16x8_t*>(&As[sa[i]]) = ra[i];
+    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<bf16x8_t*>(&As[sa[i]]) = ra[st][i];
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) *reinterpret_cast<bf16x8_t*>(&Bs[sb[i]]) = rb[i];
+    for (int i = 0; i < B_CH; ++i) *reinterpret_cast<bf16x8_t*>(&Bs[sb[i]]) = rb[st][i];
   };
 
   const int wm = wave % WM, wn = wave / WM;
@@ -407,12 +434,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(GemmArgs g) {
   const int kh = (lane >> 5) * 8;
   const uint16_t* a_base = &As[(wm * TM + r32) * LD + kh];
   const uint16_t* b_base = &Bs[(wn * TN + r32) * LD + kh];
-  gload(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    sstore();
-    __syncthreads();
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  auto compute = [&]() {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8_t a[FM], b[FN];
@@ -428,29 +450,71 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(GemmArgs g) {
         for (int f = 0; f < FN; ++f)
           acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
     }
+  };
+#pragma unroll
+  for (int st = 0; st < PF; ++st)
+    if (st < nk) gload(st, st * BK);
+  // the loop body is unrolled PF times so the register stage index is constant
+  for (int kt = 0; kt < nk; kt += PF) {
+#pragma unroll
+    for (int st = 0; st < PF; ++st) {
+      if (kt + st < nk) {
+        __syncthreads();
+        sstore(st);
+        __syncthreads();
+        if (kt + st + PF < nk) gload(st, (kt + st + PF) * BK);
+        compute();
+      }
+    }
   }
 
-  // C layout of 32x32: element r of lane l is row (r/4)*8 + (l/32)*4 + r%4, column l%32
+  // Epilogue. C layout of 32x32: element r of lane l is row (r/4)*8 +
+  // (l/32)*4 + r%4, column l%32 of the fragment. Each lane turns its values
+  // into bf16 outputs (gate-up: bf16(silu(bf16 g) * bf16 u); down: bf16(acc *
+  // w[p])) and writes them into the LDS tile; then every thread copies 16-byte
+  // row segments to their output rows.
+  constexpr int PR = BM / NP;  // rows per pass
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int pass = 0; pass < NP; ++pass) {
+    __syncthreads();  // operand buffers / previous pass no longer read
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rr = wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      if (rr >= rows) continue;
-      const int q = row0 + rr;
-      if (EPI == EPI_GATEUP) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int pp = 0; pp < FN / 2; ++pp) {
-          const int c = n0 + wn * (TN / 2) + pp * 32 + r32;
-          if (c < g.n_out) store_gateup(g, q, c, acc[i][2 * pp][r], acc[i][2 * pp + 1][r]);
-        }
-      } else {
+      for (int r = 0; r < 16; ++r) {
+        const int rr = wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (rr / PR != pass) continue;
+        uint16_t* crow = smem + (rr - pass * PR) * CLD;
+        if (EPI == EPI_GATEUP) {
 #pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const int c = n0 + wn * TN + f * 32 + r32;
-          if (c < g.n_out) store_plain<EPI>(g, q, c, acc[i][f][r]);
+          for (int pp = 0; pp < FN / 2; ++pp) {
+#pragma clang fp contract(off)
+            const float gb = round_bf16(acc[i][2 * pp][r]);  // N1
+            const float ub = round_bf16(acc[i][2 * pp + 1][r]);
+            crow[wn * (TN / 2) + pp * 32 + r32] = (uint16_t)f32_to_bf16(silu_cw(gb) * ub);
+          }
+        } else {
+          const float w = row_w[rr];
+#pragma unroll
+          for (int f = 0; f < FN; ++f) {
+#pragma clang fp contract(off)
+            float y = acc[i][f][r];
+            if (g.pair_w != nullptr) y = y * w;  // N2: weight on the accumulator
+            crow[wn * TN + f * 32 + r32] = (uint16_t)f32_to_bf16(y);
+          }
         }
       }
+    }
+    __syncthreads();
+    constexpr int CH = OUT_COLS / 8;  // 16-byte chunks per row
+    for (int idx = tid; idx < PR * CH; idx += NT) {
+      const int lr = idx / CH, c8 = (idx - lr * CH) * 8;
+      const int rr = pass * PR + lr;
+      const int dest = row_dest[rr];
+      const int col = n0 + c8;
+      if (dest < 0 || col >= g.n_out) continue;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + lr * CLD + c8);
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(g.out) + (size_t)dest * g.n_out +
+                                  col) = v;
     }
   }
 }
