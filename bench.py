@@ -49,6 +49,30 @@ def algorithmic_work(cfg, offsets):
     return gu, dn, touched
 
 
+def measured_traffic(workload):
+    """HBM bytes per gate-up launch from the committed rocprofv3 counter runs.
+
+    Only valid while the GEMM source is the one the counters were taken on
+    (its sha256 is recorded in the summary); otherwise None.
+    """
+    import hashlib
+    import re
+    if workload != 2:
+        return None
+    summary = os.path.join(ROOT, "profiles", "decode_gateup_hbm_traffic.md")
+    src = os.path.join(ROOT, "mixture_experts_ffn_expert_amd", "csrc", "gemm.hip")
+    try:
+        txt = open(summary).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", txt)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", txt)
+    if not m_sha or not m_val or m_sha.group(1) != sha:
+        return None
+    return int(m_val.group(1))
+
+
 def cpu_baseline(d, sample_tokens):
     """The oracle (as it stands) on the first `sample_tokens` tokens."""
     import oracle
@@ -174,6 +198,7 @@ def main():
         achieved = gu["flops"] / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+    roof["traffic"] = measured_traffic(args.workload)
     roof["kernel"] = "grouped gate-up GEMM + SiLU-mul"
     roof["algorithmic"] = {"bytes_per_launch": gu["bytes"], "flops_per_launch": gu["flops"],
                            "touched_experts": touched}
