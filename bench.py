@@ -142,6 +142,8 @@ def main():
     w_g = bf(d["w_g"]) if "w_g" in d else None
     T, H, E, K, I = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I
     bufs = {}
+    ws_bytes = moe.moe_route_workspace_bytes(T, E, K)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream()
     ev = []
 
@@ -149,7 +151,7 @@ def main():
         logits = moe.moe_router_logits(x, w_r, bias, bufs.get("logits"))
         bufs["logits"] = logits
         ids, w, off, sp = moe.moe_route(logits, K, bufs.get("ids"), bufs.get("w"),
-                                        bufs.get("offsets"), bufs.get("sorted"))
+                                        bufs.get("offsets"), bufs.get("sorted"), ws)
         bufs.update(ids=ids, w=w, offsets=off, sorted=sp)
         if record:
             e0 = torch.cuda.Event(enable_timing=True)

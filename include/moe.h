@@ -96,7 +96,10 @@ moe_status moe_init(void);
 moe_status moe_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
                              const float* bias, float* out, moe_stream_t stream);
 
-/* Bytes of device workspace moe_route needs (currently 0: pass NULL/0). */
+/* Bytes of device workspace moe_route needs for (T, E, K): 0 up to 4096
+ * routed pairs (T*K), else 4 bytes per (4096-pair segment, expert). The
+ * workspace is scratch owned by the caller, 4-byte aligned, and may be
+ * reused across calls on one stream; its contents on entry do not matter. */
 size_t moe_route_workspace_bytes(int T, int E, int K);
 
 /*
@@ -113,6 +116,7 @@ size_t moe_route_workspace_bytes(int T, int E, int K);
  *   sorted_pairs   int32 [T*K]: pair indices p = t*K + k grouped by expert,
  *                  increasing p within an expert
  *   ws, ws_bytes   workspace of at least moe_route_workspace_bytes(T,E,K)
+ *                  bytes (MOE_E_WORKSPACE if smaller; NULL allowed when 0)
  * Results are bit-identical run to run (no atomics decide an order).
  */
 moe_status moe_route(const float* logits, int T, int E, int K, int32_t* topk_ids,

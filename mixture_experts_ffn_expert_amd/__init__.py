@@ -164,6 +164,9 @@ def moe_route(logits, K, topk_ids=None, topk_w=None, expert_offsets=None, sorted
     _need(topk_w, "topk_w", torch.float32, shape=(T, K))
     _need(expert_offsets, "expert_offsets", torch.int32, shape=(E + 1,))
     _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * K,))
+    need = moe_route_workspace_bytes(T, E, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().moe_route(_ptr(logits), T, E, K, _ptr(topk_ids), _ptr(topk_w),
                             _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(workspace), ws_bytes,
@@ -273,10 +276,12 @@ def moe_layer(x, w_r, w_gu, w_d, K, router_bias=None, w_gu_s=None, w_d_s=None, w
         return b[key]
 
     logits = moe_router_logits(x, w_r, router_bias, buf("logits", (T, E), torch.float32), stream)
+    ws_bytes = moe_route_workspace_bytes(T, E, K)
+    ws = buf("route_ws", (ws_bytes,), torch.uint8) if ws_bytes else None
     ids, w, off, sp = moe_route(logits, K, buf("ids", (T, K), torch.int32),
                                 buf("w", (T, K), torch.float32),
                                 buf("offsets", (E + 1,), torch.int32),
-                                buf("sorted", (T * K,), torch.int32), stream=stream)
+                                buf("sorted", (T * K,), torch.int32), ws, stream=stream)
     act = moe_grouped_gemm_gateup_silu(x, w_gu, sp, off, K, buf("act", (T * K, I), torch.bfloat16),
                                        stream)
     eo = moe_grouped_gemm_down(act, w_d, sp, off, w, buf("expert_out", (T * K, H), torch.bfloat16),

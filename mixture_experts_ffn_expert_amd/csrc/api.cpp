@@ -133,10 +133,8 @@ moe_status moe_router_logits(const uint16_t* x, int T, int H, const uint16_t* w,
 }
 
 size_t moe_route_workspace_bytes(int T, int E, int K) {
-  (void)T;
-  (void)E;
-  (void)K;
-  return 0;
+  if (T <= 0 || E < 1 || K < 1) return 0;
+  return moe::route_workspace_bytes(T, E, K);
 }
 
 moe_status moe_route(const float* logits, int T, int E, int K, int32_t* topk_ids, float* topk_w,
@@ -153,9 +151,11 @@ moe_status moe_route(const float* logits, int T, int E, int K, int32_t* topk_ids
   if (ws_bytes < moe_route_workspace_bytes(T, E, K))
     return fail(MOE_E_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, ws_bytes,
                 moe_route_workspace_bytes(T, E, K));
-  (void)ws;
   REQUIRE_NONNULL(fn, expert_offsets);
   if (T == 0) return MOE_OK;  // nothing routed; no output is written
+  if (moe_route_workspace_bytes(T, E, K) > 0 && (ws == nullptr || (uintptr_t)ws % 4 != 0))
+    return fail(MOE_E_WORKSPACE, "%s: ws is NULL or not 4-byte aligned (%zu bytes needed)", fn,
+                moe_route_workspace_bytes(T, E, K));
   REQUIRE_NONNULL(fn, logits);
   REQUIRE_NONNULL(fn, topk_ids);
   REQUIRE_NONNULL(fn, topk_w);
@@ -163,7 +163,7 @@ moe_status moe_route(const float* logits, int T, int E, int K, int32_t* topk_ids
   moe_status st = check_device(fn);
   if (st != MOE_OK) return st;
   return hip_status(fn, moe::launch_route(logits, T, E, K, topk_ids, topk_w, expert_offsets,
-                                          sorted_pairs, static_cast<hipStream_t>(stream)));
+                                          sorted_pairs, ws, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w_gu,

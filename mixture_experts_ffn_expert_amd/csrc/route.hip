@@ -12,12 +12,13 @@
 //   lowest expert id holding it, so ties go to the lower id; lane k keeps the
 //   k-th logit, computes e_k = exp(l_k - l_0), every lane forms the same
 //   sequential f32 sum, lane k divides.
-// Kernel 2 (group_kernel): one workgroup of 8 waves. Wave w owns a
-//   contiguous segment of pairs. (i) per-wave expert histogram in LDS,
-//   (ii) exclusive scan over experts of the totals and per-wave bases,
-//   (iii) each wave walks its segment in order, 64 pairs at a time, ranks
-//   equal experts inside the 64 by ballots, and scatters. No atomic decides
-//   an order, so the permutation is the stable one and is reproducible.
+// Grouping (group_kernel for up to 4096 pairs, else the count / scan /
+//   scatter kernels over 4096-pair segments): (i) per-wave expert histograms
+//   in LDS, (ii) an exclusive scan over experts (and segments) gives every
+//   wave its first output position per expert, (iii) each wave walks its part
+//   in order, 64 pairs at a time, ranks equal experts inside the 64 by
+//   ballots, and scatters. No atomic decides an order, so the permutation is
+//   the stable one and is reproducible.
 #include "device_math.h"
 #include "launch.h"
 
@@ -109,74 +110,32 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 }
 
 constexpr int kGroupWaves = 8;
+// Pairs per workgroup segment of the multi-workgroup grouping (and the
+// largest pair count the single-workgroup kernel handles).
+constexpr int kGroupSeg = 4096;
 
-__global__ __launch_bounds__(kGroupWaves * 64) void group_kernel(const int32_t* __restrict__ ids,
-                                                                 int P, int E,
-                                                                 int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ sorted) {
-  __shared__ int cur[kGroupWaves][kMaxE];  // per-wave counts, then per-wave cursors
-  __shared__ int wave_tot[kGroupWaves * 64 / 64];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  for (int i = tid; i < kGroupWaves * kMaxE; i += blockDim.x) (&cur[0][0])[i] = 0;
-  __syncthreads();
-
-  const int seg = (P + kGroupWaves - 1) / kGroupWaves;
-  const int beg = min(P, wave * seg);
-  const int end = min(P, beg + seg);
-  // (i) per-wave histogram (counts commute, so LDS atomics are fine here)
-  for (int p = beg + lane; p < end; p += 64) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cur[wave][e], 1);
-  }
-  __syncthreads();
-
-  // (ii) totals per expert and their exclusive scan; thread i owns experts
-  // [i*per, (i+1)*per) in order.
-  const int nthreads = kGroupWaves * 64;
-  const int per = (E + nthreads - 1) / nthreads;
-  const int e0 = min(E, tid * per);
-  const int e1 = min(E, e0 + per);
-  int local = 0;
-  for (int e = e0; e < e1; ++e)
-    for (int w = 0; w < kGroupWaves; ++w) local += cur[w][e];
-  // inclusive scan of `local` across the block
-  int incl = local;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    int o = __shfl_up(incl, m);
-    if (lane >= m) incl += o;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int wave_base = 0;
-  for (int w = 0; w < wave; ++w) wave_base += wave_tot[w];
-  int run = wave_base + incl - local;  // exclusive prefix of this thread's first expert
-  for (int e = e0; e < e1; ++e) {
-    offsets[e] = run;
-    int c = run;
-    for (int w = 0; w < kGroupWaves; ++w) {
-      int n = cur[w][e];
-      cur[w][e] = c;  // cursor of wave w for expert e
-      c += n;
-    }
-    run = c;
-  }
-  if (tid == 0) offsets[E] = P;
-  __syncthreads();
-
-  // (iii) in-order stable scatter; ranks inside each group of 64 by ballots
+// Stable in-order scatter of pairs [beg, end) by one workgroup. cur[w][e]
+// holds, on entry, wave w's first output position for expert e; wave w owns
+// the w-th contiguous part of the segment and walks it 64 pairs at a time,
+// ranking equal experts inside the 64 with ballots over the id bits.
+__device__ __forceinline__ void scatter_segment(const int32_t* __restrict__ ids, int beg, int end,
+                                                int E, int (*cur)[kMaxE],
+                                                int32_t* __restrict__ sorted) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int seg = (end - beg + kGroupWaves - 1) / kGroupWaves;
+  const int wb = min(end, beg + wave * seg);
+  const int we = min(end, wb + seg);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  for (int base = beg; base < end; base += 64) {
+  for (int base = wb; base < we; base += 64) {
     const int p = base + lane;
-    int e = (p < end) ? ids[p] : 0;
-    const bool valid = p < end && (unsigned)e < (unsigned)E;  // ids come from topk_kernel
+    int e = (p < we) ? ids[p] : 0;
+    const bool valid = p < we && (unsigned)e < (unsigned)E;  // ids come from topk_kernel
     if (!valid) e = 0;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
-      uint64_t m = __ballot(valid && ((e >> b) & 1));
+      const uint64_t m = __ballot(valid && ((e >> b) & 1));
       peers &= ((e >> b) & 1) ? m : ~m;
     }
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -185,18 +144,169 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_kernel(const int32_t* 
     if (valid) pos = cur[wave][e] + rank;
     __builtin_amdgcn_wave_barrier();
     // the highest lane of each peer group advances the cursor
-    const bool last = valid && ((peers >> lane) == 1ull);
-    if (last) cur[wave][e] = pos + 1;
+    if (valid && (peers >> lane) == 1ull) cur[wave][e] = pos + 1;
     __builtin_amdgcn_wave_barrier();
     if (valid) sorted[pos] = p;
   }
 }
 
+// Per-wave expert counts of the waves' parts of segment [beg, end).
+__device__ __forceinline__ void count_segment(const int32_t* __restrict__ ids, int beg, int end,
+                                              int E, int (*cur)[kMaxE]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kGroupWaves * kMaxE; i += blockDim.x) (&cur[0][0])[i] = 0;
+  __syncthreads();
+  const int seg = (end - beg + kGroupWaves - 1) / kGroupWaves;
+  const int wb = min(end, beg + wave * seg);
+  const int we = min(end, wb + seg);
+  // counts commute, so LDS atomics are fine here
+  for (int p = wb + lane; p < we; p += 64) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cur[wave][e], 1);
+  }
+  __syncthreads();
+}
+
+// Single workgroup: counts, the exclusive scan over experts, then the scatter.
+__global__ __launch_bounds__(kGroupWaves * 64) void group_kernel(const int32_t* __restrict__ ids,
+                                                                 int P, int E,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ sorted) {
+  __shared__ int cur[kGroupWaves][kMaxE];  // per-wave counts, then per-wave cursors
+  __shared__ int wave_tot[kGroupWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  count_segment(ids, 0, P, E, cur);
+
+  // totals per expert and their exclusive scan; thread i owns experts
+  // [i*per, (i+1)*per) in order
+  const int nthreads = kGroupWaves * 64;
+  const int per = (E + nthreads - 1) / nthreads;
+  const int e0 = min(E, tid * per);
+  const int e1 = min(E, e0 + per);
+  int local = 0;
+  for (int e = e0; e < e1; ++e)
+    for (int w = 0; w < kGroupWaves; ++w) local += cur[w][e];
+  int incl = local;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int o = __shfl_up(incl, m);
+    if (lane >= m) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int w = 0; w < wave; ++w) run += wave_tot[w];
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = run;
+    for (int w = 0; w < kGroupWaves; ++w) {
+      const int n = cur[w][e];
+      cur[w][e] = run;  // cursor of wave w for expert e
+      run += n;
+    }
+  }
+  if (tid == 0) offsets[E] = P;
+  __syncthreads();
+  scatter_segment(ids, 0, P, E, cur, sorted);
+}
+
+// Multi-workgroup grouping, step 1: expert counts of each segment of
+// kGroupSeg pairs -> cnt[b][e].
+__global__ __launch_bounds__(kGroupWaves * 64) void group_count_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ cnt) {
+  __shared__ int cur[kGroupWaves][kMaxE];
+  const int beg = blockIdx.x * kGroupSeg;
+  const int end = min(P, beg + kGroupSeg);
+  count_segment(ids, beg, end, E, cur);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) n += cur[w][e];
+    cnt[(size_t)blockIdx.x * E + e] = n;
+  }
+}
+
+// Step 2 (one workgroup): expert offsets, and cnt[b][e] replaced by segment
+// b's first output position for expert e.
+__global__ __launch_bounds__(1024) void group_scan_kernel(int32_t* __restrict__ cnt, int nseg,
+                                                          int P, int E,
+                                                          int32_t* __restrict__ offsets) {
+  __shared__ int wave_tot[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int e = tid;  // E <= 1024: one expert per thread
+  int tot = 0;
+  if (e < E)
+    for (int b = 0; b < nseg; ++b) tot += cnt[(size_t)b * E + e];
+  int incl = tot;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int o = __shfl_up(incl, m);
+    if (lane >= m) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int run = incl - tot;
+  for (int w = 0; w < wave; ++w) run += wave_tot[w];
+  if (e < E) {
+    offsets[e] = run;
+    for (int b = 0; b < nseg; ++b) {
+      const int n = cnt[(size_t)b * E + e];
+      cnt[(size_t)b * E + e] = run;
+      run += n;
+    }
+  }
+  if (tid == 0) offsets[E] = P;
+}
+
+// Step 3: each segment scatters its pairs in order from its own positions.
+__global__ __launch_bounds__(kGroupWaves * 64) void group_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ base,
+    int32_t* __restrict__ sorted) {
+  __shared__ int cur[kGroupWaves][kMaxE];
+  const int beg = blockIdx.x * kGroupSeg;
+  const int end = min(P, beg + kGroupSeg);
+  count_segment(ids, beg, end, E, cur);
+  // wave w's cursor = segment base + counts of waves before w (in order)
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = base[(size_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) {
+      const int n = cur[w][e];
+      cur[w][e] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
+  scatter_segment(ids, beg, end, E, cur, sorted);
+}
+
+size_t route_workspace_bytes(int T, int E, int K) {
+  const long long P = (long long)T * K;
+  if (P <= kGroupSeg) return 0;
+  const long long nseg = (P + kGroupSeg - 1) / kGroupSeg;
+  return (size_t)(nseg * E * 4);
+}
+
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w,
-                        int32_t* offsets, int32_t* sorted, hipStream_t s) {
+                        int32_t* offsets, int32_t* sorted, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupWaves * 64), 0, s, ids, T * K, E, offsets,
-                     sorted);
+  const int P = T * K;
+  if (P <= kGroupSeg) {
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupWaves * 64), 0, s, ids, P, E, offsets,
+                       sorted);
+  } else {
+    const int nseg = (P + kGroupSeg - 1) / kGroupSeg;
+    int32_t* cnt = static_cast<int32_t*>(ws);
+    hipLaunchKernelGGL(group_count_kernel, dim3(nseg), dim3(kGroupWaves * 64), 0, s, ids, P, E,
+                       cnt);
+    hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, nseg, P, E, offsets);
+    hipLaunchKernelGGL(group_scatter_kernel, dim3(nseg), dim3(kGroupWaves * 64), 0, s, ids, P, E,
+                       cnt, sorted);
+  }
   return hipGetLastError();
 }
 

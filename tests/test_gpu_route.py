@@ -58,3 +58,21 @@ def test_route_is_deterministic(gpu_lib):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("T,E,K", [(513, 128, 8), (512, 128, 8), (3000, 1024, 32), (8192, 256, 8)])
+def test_route_multi_segment_grouping_with_dirty_workspace(gpu_lib, T, E, K):
+    """Pair counts around and far above one 4096-pair segment; the caller's
+    workspace starts full of garbage and the result must not depend on it."""
+    g = np.random.Generator(np.random.PCG64(T + E + K))
+    l = g.standard_normal((T, E)).astype(F32)
+    l[:, :3] += 4.0                        # a few hot experts: long, uneven segments
+    need = gpu_lib.moe_route_workspace_bytes(T, E, K)
+    ws = torch.full((max(need, 16),), 0xA5, dtype=torch.uint8, device=DEV)
+    out = [bits(t).copy() for t in gpu_lib.moe_route(to_dev(l), K, workspace=ws)]
+    torch.cuda.synchronize()
+    r_ids, r_w, r_off, r_sp = O.route(l, K)
+    assert_bits_equal(out[0], r_ids, "ids")
+    assert_bits_equal(out[1], r_w, "weights")
+    assert_bits_equal(out[2], r_off, "offsets")
+    assert_bits_equal(out[3], r_sp, "sorted_pairs")
