@@ -110,6 +110,80 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& g, int BM, int slot, i
   return false;
 }
 
+// Expert-major block order for the tiled kernel. Logical block L is mapped
+// to (expert e, row tile mt of e, column block nb): experts in order; inside
+// an expert, groups of GM row tiles (outer), column blocks (middle), row
+// tiles of the group (inner). Consecutive blocks then reuse one weight tile
+// across GM row tiles and one activation tile across the column blocks.
+// Called by a whole wavefront; the result is uniform across it.
+__device__ __forceinline__ bool find_block(const GemmArgs& g, int BM, int GM, int L, int& e,
+                                           int& row0, int& rows, int& nb) {
+  if (g.offsets == nullptr) {  // one expert, P rows
+    const int mt_e = (g.P + BM - 1) / BM;
+    if (L >= mt_e * g.nblk) return false;
+    e = 0;
+    const int full = mt_e / GM;
+    int mg = L / (GM * g.nblk), gm = GM, rem = L - mg * GM * g.nblk;
+    if (mg >= full) {
+      mg = full;
+      gm = mt_e - full * GM;
+      rem = L - full * GM * g.nblk;
+    }
+    nb = rem / gm;
+    const int mt = mg * GM + (rem - nb * gm);
+    row0 = mt * BM;
+    rows = min(BM, g.P - row0);
+    return true;
+  }
+  const int lane = threadIdx.x & 63;
+  int before = 0;
+  for (int base = 0; base < g.E; base += 64) {
+    const int ex = base + lane;
+    int o0 = 0, cnt = 0;
+    if (ex < g.E) {
+      o0 = min(max(g.offsets[ex], 0), g.P);
+      const int o1 = min(max(g.offsets[ex + 1], 0), g.P);
+      cnt = max(0, o1 - o0);
+    }
+    const int mt_e = (cnt + BM - 1) / BM;
+    const int nbl = mt_e * g.nblk;
+    int incl = nbl;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int o = __shfl_up(incl, m);
+      if (lane >= m) incl += o;
+    }
+    const int first = before + incl - nbl;
+    const bool mine = nbl > 0 && L >= first && L < first + nbl;
+    const uint64_t hit = __ballot(mine);
+    if (hit) {
+      const int src = __ffsll((long long)hit) - 1;
+      e = __shfl(ex, src);
+      const int f = __shfl(first, src);
+      const int oo = __shfl(o0, src);
+      const int cc = __shfl(cnt, src);
+      const int mte = __shfl(mt_e, src);
+      const int local = L - f;
+      const int full = mte / GM;
+      int mg = local / (GM * g.nblk), gm = GM, rem = local - mg * GM * g.nblk;
+      if (mg >= full) {
+        mg = full;
+        gm = mte - full * GM;
+        rem = local - full * GM * g.nblk;
+      }
+      nb = rem / gm;
+      const int mt = mg * GM + (rem - nb * gm);
+      row0 = oo + mt * BM;
+      rows = min(BM, cc - mt * BM);
+      return true;
+    }
+    before += __shfl(incl, 63);
+  }
+  return false;
+}
+
+constexpr int kXcds = 8;
+
 // Epilogue of one output element (row q of the problem, column c).
 template <int EPI>
 __device__ __forceinline__ void store_plain(const GemmArgs& g, int q, int c, float acc) {
@@ -302,8 +376,9 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(GemmArgs g) {
 // 16-byte fragment reads). The next k step is loaded into registers while
 // the current one is multiplied (v_mfma_f32_32x32x16_bf16).
 // ---------------------------------------------------------------------------
-template <int EPI, int BM, int BN, int BK, int WM, int WN, int PF = 1>
-__global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(GemmArgs g) {
+template <int EPI, int BM, int BN, int BK, int WM, int WN, int PF = 1, int MINB = 1, int GM = 0,
+          bool XCD = false>
+__global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
   constexpr int NT = 64 * WM * WN;             // threads
   constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
   constexpr int FM = TM / 32, FN = TN / 32;    // 32x32 fragments per wave
@@ -326,23 +401,35 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_kernel(GemmArgs g) {
   uint16_t* Bs = smem + BM * LD;
   __shared__ int row_dest[BM];      // output row of each tile row (-1: none)
   __shared__ float row_w[BM];       // routing weight of each tile row (down)
-  __shared__ int tile_info[3];
+  __shared__ int tile_info[4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int slot = blockIdx.x / g.nblk;
-  const int nb = blockIdx.x - slot * g.nblk;
+  int L = blockIdx.x;
+  if (XCD) {  // each XCD (every 8th workgroup, own L2) takes a contiguous run
+    const int per = gridDim.x / kXcds;
+    L = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  }
   if (wave == 0) {
-    int e = 0, row0 = 0, rows = 0;
-    if (!find_tile(g, BM, slot, e, row0, rows)) rows = 0;
+    int e = 0, row0 = 0, rows = 0, nb = 0;
+    bool ok;
+    if (GM > 0) {
+      ok = find_block(g, BM, GM, L, e, row0, rows, nb);
+    } else {
+      const int slot = L / g.nblk;
+      nb = L - slot * g.nblk;
+      ok = find_tile(g, BM, slot, e, row0, rows);
+    }
+    if (!ok) rows = 0;
     if (lane == 0) {
       tile_info[0] = e;
       tile_info[1] = row0;
       tile_info[2] = rows;
+      tile_info[3] = nb;
     }
   }
   __syncthreads();
-  const int e = tile_info[0], row0 = tile_info[1], rows = tile_info[2];
+  const int e = tile_info[0], row0 = tile_info[1], rows = tile_info[2], nb = tile_info[3];
   if (rows <= 0) return;
   const int n0 = nb * OUT_COLS;
   for (int rr = tid; rr < BM; rr += NT) {
@@ -527,6 +614,14 @@ static inline int slots_for(int P, int E, int BM, bool grouped) {
   return grouped ? full + (E < P ? E : P) : full;
 }
 
+// Grid of the tiled kernel: slots x nblk, rounded up to a multiple of the
+// XCD count when the XCD renumbering is on.
+static inline unsigned grid_tiled(const GemmArgs& g, bool xcd) {
+  long long n = (long long)g.slots * g.nblk;
+  if (xcd) n = (n + kXcds - 1) / kXcds * kXcds;
+  return (unsigned)n;
+}
+
 // Grid of slots x nblk workgroups. Consecutive workgroups take adjacent
 // column blocks of one expert, i.e. adjacent weight rows: the chip streams
 // one contiguous region at a time, which measured faster than pinning an
@@ -572,10 +667,27 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
       }
     }
   } else {
+    // many rows per expert: LDS tiles of 128 rows x 128 weight rows. Orders
+    // measured at the prefill (256 rows per expert) and skewed (hot experts
+    // of up to 8191 rows) workloads: with a few row tiles per expert the
+    // gate-up GEMM reuses each weight tile across the expert's row tiles on
+    // one XCD (expert-major order, groups of 8 row tiles); with many row
+    // tiles the plain order is faster, and it is for the down GEMM too.
     constexpr int BM = 128, BN = 128;
-    g.nblk = (g.n_out + (EPI == EPI_GATEUP ? BN / 2 : BN) - 1) / (EPI == EPI_GATEUP ? BN / 2 : BN);
+    constexpr int OC = (EPI == EPI_GATEUP) ? BN / 2 : BN;
+    g.nblk = (g.n_out + OC - 1) / OC;
     g.slots = slots_for(g.P, g.E, BM, grouped);
-    hipLaunchKernelGGL((tiled_kernel<EPI, BM, BN, 64, 2, 2>), dim3(grid_for(g)), dim3(256), 0, s, g);
+    if constexpr (EPI == EPI_GATEUP) {
+      if (avg_rows <= 384.0)
+        hipLaunchKernelGGL((tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 1, 8, true>),
+                           dim3(grid_tiled(g, true)), dim3(256), 0, s, g);
+      else
+        hipLaunchKernelGGL((tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 1, 0, false>),
+                           dim3(grid_tiled(g, false)), dim3(256), 0, s, g);
+    } else {
+      hipLaunchKernelGGL((tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 4, 0, false>),
+                         dim3(grid_tiled(g, false)), dim3(256), 0, s, g);
+    }
   }
   return hipGetLastError();
   }
