@@ -42,13 +42,19 @@ __device__ __forceinline__ float lane_f32(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
-                                                   int K, int32_t* __restrict__ ids,
-                                                   float* __restrict__ w) {
+// Inverse of order_key for keys of non-NaN floats.
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Top-K of one token's E logits by one wavefront; lane k < K writes ids[k]
+// and w[k]. The selected logit is recovered from its key: it equals the
+// logit except that -0 reads as +0, which changes no weight (x - (+-0) and
+// (+-0) - (+-0) give the same exp argument up to the sign of zero, and
+// exp(+-0) = 1).
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int K,
+                                           int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole wave leaves together
-  const float* row = logits + (size_t)t * E;
   const int nper = (E + 63) >> 6;
   uint32_t key[kMaxPerLane];
 #pragma unroll
@@ -63,7 +69,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     }
     key[j] = kj;
   }
-  float my_val = 0.0f;  // lane k keeps the k-th selected logit
+  uint32_t my_key = 0;  // lane k keeps the k-th selected key
   int my_id = 0;
   for (int k = 0; k < K; ++k) {
     uint32_t m = 0;
@@ -85,12 +91,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     for (int j = 0; j < kMaxPerLane; ++j)
       if (sel == lane + 64 * j) key[j] = 0;  // taken
     if (lane == k) {
-      float x = row[sel];
-      my_val = (x != x) ? -__builtin_inff() : x;
+      my_key = M;
       my_id = sel;
     }
   }
   // renormalised weights: e_k = exp(l_k - l_0), S = ((e_0 + e_1) + ...), w_k = e_k / S
+  const float my_val = key_value(my_key);
   const float top = lane_f32(my_val, 0);
   float ek;
   {
@@ -104,9 +110,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     S = S + lane_f32(ek, k);
   }
   if (lane < K) {
-    ids[(size_t)t * K + lane] = my_id;
-    w[(size_t)t * K + lane] = __fdiv_rn(ek, S);
+    ids[lane] = my_id;
+    w[lane] = __fdiv_rn(ek, S);
   }
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int K, int32_t* __restrict__ ids,
+                                                   float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave leaves together
+  topk_token(logits + (size_t)t * E, E, K, ids + (size_t)t * K, w + (size_t)t * K);
 }
 
 constexpr int kGroupWaves = 8;
@@ -118,7 +132,7 @@ constexpr int kGroupSeg = 4096;
 // holds, on entry, wave w's first output position for expert e; wave w owns
 // the w-th contiguous part of the segment and walks it 64 pairs at a time,
 // ranking equal experts inside the 64 with ballots over the id bits.
-__device__ __forceinline__ void scatter_segment(const int32_t* __restrict__ ids, int beg, int end,
+__device__ __forceinline__ void scatter_segment(const int32_t* ids, int beg, int end,
                                                 int E, int (*cur)[kMaxE],
                                                 int32_t* __restrict__ sorted) {
   const int lane = threadIdx.x & 63;
@@ -151,7 +165,7 @@ __device__ __forceinline__ void scatter_segment(const int32_t* __restrict__ ids,
 }
 
 // Per-wave expert counts of the waves' parts of segment [beg, end).
-__device__ __forceinline__ void count_segment(const int32_t* __restrict__ ids, int beg, int end,
+__device__ __forceinline__ void count_segment(const int32_t* ids, int beg, int end,
                                               int E, int (*cur)[kMaxE]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -293,8 +307,8 @@ size_t route_workspace_bytes(int T, int E, int K) {
 
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                         int32_t* offsets, int32_t* sorted, void* ws, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
   const int P = T * K;
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
   if (P <= kGroupSeg) {
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupWaves * 64), 0, s, ids, P, E, offsets,
                        sorted);

@@ -37,6 +37,7 @@ def test_route_workloads_bit_exact(gpu_lib, n, seed):
 
 
 @pytest.mark.parametrize("T,E,K", [(777, 37, 1), (777, 37, 5), (300, 37, 32), (129, 1024, 32),
+                                   (64, 1024, 32), (65, 37, 5), (64, 64, 64 // 2),
                                    (64, 1, 1), (1, 8, 8), (5000, 256, 8)])
 def test_route_ties_nan_inf(gpu_lib, T, E, K):
     g = np.random.Generator(np.random.PCG64(T * 1000 + E + K))
