@@ -607,6 +607,264 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// tiled_dma_kernel: BM x BN block tile (BN weight rows), WM x WN waves, k step
+// 64, NS-stage LDS ring filled by direct-to-LDS buffer loads
+// (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at M0 + 16*l; an
+// out-of-range offset writes zeros). Stage s+NS-1 is loading while stage s is
+// multiplied, with no register staging. LDS rows are 128 bytes, unpadded;
+// 16-byte chunk c of tile row r sits in slot c ^ ((r >> 1) & 7), which keeps
+// the 16-byte fragment reads of 16 consecutive rows on distinct banks.
+//
+// The loads are issued from inline assembly and the waits are explicit
+// (s_waitcnt vmcnt(N) lgkmcnt(0); s_barrier): the compiler cannot tell which
+// ring slot a direct-to-LDS load writes and would otherwise wait for every
+// load in flight before each barrier.
+// ---------------------------------------------------------------------------
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ i32x4_t raw_rsrc(const void* base, uint32_t bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  i32x4_t r = {(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)bytes, 0x00020000};
+  return r;
+}
+
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector loads are in flight and all its
+// LDS reads are done, then barrier. Memory-clobbering, so no LDS access
+// moves across it.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <int EPI, int BM, int BN, int WM, int WN, int NS, int GM = 0, bool XCD = false>
+__global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
+  constexpr int BK = 64;
+  constexpr int NW = WM * WN;
+  constexpr int NT = 64 * NW;
+  constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
+  constexpr int FM = TM / 32, FN = TN / 32;    // 32x32 fragments per wave
+  constexpr int ROWB = BK * 2;                 // bytes per tile row (128)
+  constexpr int STAGE = (BM + BN) * ROWB;      // bytes per ring slot
+  constexpr int IPW = (BM + BN) / 8 / NW;      // 1 KiB loads per wave per stage
+  constexpr int OUT_COLS = (EPI == EPI_GATEUP) ? BN / 2 : BN;
+  constexpr int CLD = OUT_COLS + 8;            // output staging row (elements)
+  static_assert(IPW * 8 * NW == BM + BN, "loads per wave");
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "swizzle period");
+  static_assert(EPI != EPI_GATEUP || FN % 2 == 0, "gate-up pairs fragments");
+  static_assert(EPI != EPI_F32, "logits use the streaming kernel");
+  static_assert(BM * CLD * 2 <= NS * STAGE, "output staging fits the ring");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE];
+  __shared__ int row_dest[BM];
+  __shared__ float row_w[BM];
+  __shared__ int tile_info[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave == 0) {
+    int L = blockIdx.x;
+    if (XCD) {  // each XCD (every 8th workgroup, own L2) takes a contiguous run
+      const int per = gridDim.x / kXcds;
+      L = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    }
+    int e = 0, row0 = 0, rows = 0, nb = 0;
+    bool ok;
+    if (GM > 0) {
+      ok = find_block(g, BM, GM, L, e, row0, rows, nb);
+    } else {
+      const int slot = L / g.nblk;
+      nb = L - slot * g.nblk;
+      ok = find_tile(g, BM, slot, e, row0, rows);
+    }
+    if (!ok) rows = 0;
+    if (lane == 0) {
+      tile_info[0] = e;
+      tile_info[1] = row0;
+      tile_info[2] = rows;
+      tile_info[3] = nb;
+    }
+  }
+  __syncthreads();
+  const int e = tile_info[0], row0 = tile_info[1], rows = tile_info[2], nb = tile_info[3];
+  if (rows <= 0) return;
+  const int n0 = nb * OUT_COLS;
+  for (int rr = tid; rr < BM; rr += NT) {
+    int dest = -1;
+    float wgt = 1.0f;
+    if (rr < rows) {
+      const int q = row0 + rr;
+      dest = q;
+      if (EPI == EPI_DOWN && g.sorted != nullptr) {
+        dest = g.sorted[q];
+        if (dest < 0 || dest >= g.P) dest = -1;
+      }
+      if (EPI == EPI_DOWN && g.pair_w != nullptr && dest >= 0) wgt = g.pair_w[dest];
+    }
+    row_dest[rr] = dest;
+    row_w[rr] = wgt;
+  }
+
+  const i32x4_t rsrc_a = raw_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
+  const i32x4_t rsrc_b =
+      raw_rsrc(g.B + (size_t)e * g.b_rows * g.kdim, (uint32_t)g.b_rows * (uint32_t)g.kdim * 2u);
+  // Load j of this wave fills tile rows [8*(wave*IPW + j), +8) of a ring
+  // slot: lane l writes slot (l%8) of row l/8, i.e. logical chunk
+  // (l%8) ^ swz(row).
+  uint32_t voff[IPW];
+  int chunk[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int r = (wave * IPW + j) * 8 + (lane >> 3);  // tile row (A rows, then B rows)
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    uint32_t ro;
+    if (r < BM) {
+      ro = (r < rows) ? a_row_off(g, row0 + r) : kOob;
+    } else {
+      const int br = r - BM;
+      int col, up = 0;
+      if (EPI == EPI_GATEUP) {
+        const int wn = br / TN, f = (br % TN) >> 5, jj = br & 31;
+        col = n0 + wn * (TN / 2) + (f >> 1) * 32 + jj;
+        up = f & 1;
+      } else {
+        col = n0 + br;
+      }
+      ro = b_row_off<EPI>(g, col, up);
+    }
+    voff[j] = ro + c * 16;
+    chunk[j] = c * 8;
+  }
+  const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  auto issue = [&](int slot, int k0) {
+    const uint32_t soff = (uint32_t)k0 * 2u;
+    const bool full = k0 + BK <= g.kdim;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int blk = wave * IPW + j;  // uniform
+      const uint32_t m0 = ring_base + slot * STAGE + blk * 1024;
+      const uint32_t vo = (full || k0 + chunk[j] < g.kdim) ? voff[j] : kOob;
+      dma16(blk * 8 < BM ? rsrc_a : rsrc_b, m0, vo, soff);
+    }
+  };
+
+  const int wm = wave % WM, wn = wave / WM;
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
+  // fragment byte offsets inside a ring slot, per k16 step kk
+  const int r32 = lane & 31;
+  const int khalf = lane >> 5;
+  uint32_t aoff[FM][BK / 16], boff[FN][BK / 16];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * TM + i * 32 + r32;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk)
+      aoff[i][kk] = r * ROWB + (((kk * 2 + khalf) ^ ((r >> 1) & 7)) * 16);
+  }
+#pragma unroll
+  for (int f = 0; f < FN; ++f) {
+    const int r = BM + wn * TN + f * 32 + r32;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk)
+      boff[f][kk] = r * ROWB + (((kk * 2 + khalf) ^ ((r >> 1) & 7)) * 16);
+  }
+  auto compute = [&](int slot) {
+    const unsigned char* sb = ring + slot * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8_t a[FM], b[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(sb + aoff[i][kk]);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) b[f] = *reinterpret_cast<const bf16x8_t*>(sb + boff[f][kk]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
+    }
+  };
+
+  const int nk = (g.kdim + BK - 1) / BK;
+  __syncthreads();  // row tables written; ring free
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st, st * BK);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed once at most (stages issued after it) * IPW of
+    // this wave's loads are still in flight; the barrier makes every wave's
+    // loads of stage kt visible and every wave done with stage kt - 1
+    const int after = min(NS - 2, nk - 1 - kt);
+    if (after >= 2)
+      wait_barrier<2 * IPW>();
+    else if (after == 1)
+      wait_barrier<IPW>();
+    else
+      wait_barrier<0>();
+    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, (kt + NS - 1) * BK);
+    compute(kt % NS);
+  }
+  wait_barrier<0>();  // ring free for the output staging
+
+  // Epilogue (as in tiled_kernel): bf16 results into LDS, then 16-byte row
+  // segments to the output rows.
+  uint16_t* smem = reinterpret_cast<uint16_t*>(ring);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      uint16_t* crow = smem + rr * CLD;
+      if (EPI == EPI_GATEUP) {
+#pragma unroll
+        for (int pp = 0; pp < FN / 2; ++pp) {
+#pragma clang fp contract(off)
+          const float gb = round_bf16(acc[i][2 * pp][r]);  // N1
+          const float ub = round_bf16(acc[i][2 * pp + 1][r]);
+          crow[wn * (TN / 2) + pp * 32 + r32] = (uint16_t)f32_to_bf16(silu_cw(gb) * ub);
+        }
+      } else {
+        const float w = row_w[rr];
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+#pragma clang fp contract(off)
+          float y = acc[i][f][r];
+          if (g.pair_w != nullptr) y = y * w;  // N2: weight on the accumulator
+          crow[wn * TN + f * 32 + r32] = (uint16_t)f32_to_bf16(y);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CH = OUT_COLS / 8;
+  for (int idx = tid; idx < BM * CH; idx += NT) {
+    const int rr = idx / CH, c8 = (idx - rr * CH) * 8;
+    const int dest = row_dest[rr];
+    const int col = n0 + c8;
+    if (dest < 0 || col >= g.n_out) continue;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + rr * CLD + c8);
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(g.out) + (size_t)dest * g.n_out + col) =
+        v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side dispatch
 // ---------------------------------------------------------------------------
 static inline int slots_for(int P, int E, int BM, bool grouped) {
@@ -666,24 +924,26 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
       }
     }
   } else {
-    // many rows per expert: LDS tiles of 128 rows x 128 weight rows. Orders
-    // measured at the prefill (256 rows per expert) and skewed (hot experts
-    // of up to 8191 rows) workloads: with a few row tiles per expert the
-    // gate-up GEMM reuses each weight tile across the expert's row tiles on
-    // one XCD (expert-major order, groups of 8 row tiles); with many row
-    // tiles the plain order is faster, and it is for the down GEMM too.
-    constexpr int BM = 128, BN = 128;
-    constexpr int OC = (EPI == EPI_GATEUP) ? BN / 2 : BN;
-    g.nblk = (g.n_out + OC - 1) / OC;
-    g.slots = slots_for(g.P, g.E, BM, grouped);
+    // many rows per expert. Gate-up: 256 x 256 tiles on 8 waves with the
+    // direct-to-LDS ring; with a few row tiles per expert (prefill) the
+    // blocks are numbered expert by expert in groups of 4 row tiles, so a
+    // weight tile is reused across them. Down: 128 x 128 register-staged
+    // tiles, plain order, 4 workgroups per CU. Chosen by measurement at the
+    // prefill (256 rows per expert) and skewed (up to 8191) workloads.
     if constexpr (EPI == EPI_GATEUP) {
+      constexpr int BM = 256, BN = 256;
+      g.nblk = (g.n_out + BN / 2 - 1) / (BN / 2);
+      g.slots = slots_for(g.P, g.E, BM, grouped);
       if (avg_rows <= 384.0)
-        hipLaunchKernelGGL((tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 1, 8, true>),
-                           dim3(grid_tiled(g, true)), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((tiled_dma_kernel<EPI, BM, BN, 2, 4, 2, 4, false>),
+                           dim3(grid_tiled(g, false)), dim3(512), 0, s, g);
       else
-        hipLaunchKernelGGL((tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 1, 0, false>),
-                           dim3(grid_tiled(g, false)), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((tiled_dma_kernel<EPI, BM, BN, 2, 4, 2, 0, false>),
+                           dim3(grid_tiled(g, false)), dim3(512), 0, s, g);
     } else {
+      constexpr int BM = 128, BN = 128;
+      g.nblk = (g.n_out + BN - 1) / BN;
+      g.slots = slots_for(g.P, g.E, BM, grouped);
       hipLaunchKernelGGL((tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 4, 0, false>),
                          dim3(grid_tiled(g, false)), dim3(256), 0, s, g);
     }
