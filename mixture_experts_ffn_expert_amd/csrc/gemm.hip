@@ -888,49 +888,69 @@ static inline unsigned grid_for(const GemmArgs& g) {
   return (unsigned)((long long)g.slots * g.nblk);
 }
 
+// Kernel shapes were chosen by measurement on MI355X at the five workload
+// shapes (decode 32 tokens / 128 experts, prefill 4096 tokens, 256 experts with
+// 16 rows each, a 512-row dense shared expert, skewed 8192 tokens).
 template <int EPI>
 static hipError_t dispatch(GemmArgs g, hipStream_t s) {
   const bool grouped = g.offsets != nullptr;
   if constexpr (EPI == EPI_F32) {
-    // logits: few columns, long k; every workgroup owns 16 rows x 16
-    // columns and its 8 waves split k (measured fastest at 32 tokens)
-    g.nblk = (g.n_out + 15) / 16;
-    g.slots = slots_for(g.P, g.E, 16, false);
-    hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 8, 4>), dim3(grid_for(g)), dim3(512), 0, s, g);
+    // logits: 128 or fewer columns, long k
+    if (g.P <= 64) {
+      // a few tokens: 16 rows x 16 columns per workgroup, k split over 8 waves
+      g.nblk = (g.n_out + 15) / 16;
+      g.slots = slots_for(g.P, g.E, 16, false);
+      hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 8, 4>), dim3(grid_for(g)), dim3(512), 0, s, g);
+    } else {
+      // many tokens: 32 rows x 64 columns, k split over 4 waves
+      g.nblk = (g.n_out + 63) / 64;
+      g.slots = slots_for(g.P, g.E, 32, false);
+      hipLaunchKernelGGL((stream_kernel<EPI, 2, 4, 4, 2>), dim3(grid_for(g)), dim3(256), 0, s, g);
+    }
     return hipGetLastError();
   } else {
-  const double avg_rows = grouped ? (double)g.P / (double)g.E : (double)g.P;
-  if (avg_rows <= 24.0) {
-    // few rows per expert: weight streaming. Shapes measured at the decode
-    // and 256-expert workloads: gate-up 16 output columns (gate + up
-    // fragments) with k split 4 ways; down 16 columns, k split 2 ways (its k
-    // is the short intermediate size) for 16-row tiles, 32 columns split 4
-    // ways for 32-row tiles.
-    if (avg_rows <= 8.0) {
-      g.slots = slots_for(g.P, g.E, 16, grouped);
-      g.nblk = (g.n_out + 15) / 16;
-      if constexpr (EPI == EPI_GATEUP)
-        hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 4, 4>), dim3(grid_for(g)), dim3(256), 0, s, g);
-      else
-        hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 2, 4>), dim3(grid_for(g)), dim3(128), 0, s, g);
-    } else {
-      g.slots = slots_for(g.P, g.E, 32, grouped);
-      if constexpr (EPI == EPI_GATEUP) {
+    const double avg_rows = grouped ? (double)g.P / (double)g.E : (double)g.P;
+    // LDS tiles pay off with hundreds of rows per expert and enough tiles to
+    // occupy the chip; everything else streams the weights.
+    const int tbm = (EPI == EPI_GATEUP) ? 256 : 128;
+    const int tcols = (EPI == EPI_GATEUP) ? 128 : 128;
+    const long long tiled_blocks = (long long)(g.P / tbm) * ((g.n_out + tcols - 1) / tcols);
+    if (avg_rows <= 24.0 || tiled_blocks < 512) {
+      if (avg_rows <= 8.0) {
+        // decode-like: 16-row tiles; gate-up 16 columns (gate + up fragments)
+        // with k split over 4 waves, down 16 columns with k split over 2
+        g.slots = slots_for(g.P, g.E, 16, grouped);
         g.nblk = (g.n_out + 15) / 16;
-        hipLaunchKernelGGL((stream_kernel<EPI, 2, 1, 4, 4>), dim3(grid_for(g)), dim3(256), 0, s, g);
+        if constexpr (EPI == EPI_GATEUP)
+          hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 4, 4>), dim3(grid_for(g)), dim3(256), 0, s,
+                             g);
+        else
+          hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 2, 4>), dim3(grid_for(g)), dim3(128), 0, s,
+                             g);
       } else {
-        g.nblk = (g.n_out + 31) / 32;
-        hipLaunchKernelGGL((stream_kernel<EPI, 2, 2, 4, 2>), dim3(grid_for(g)), dim3(256), 0, s, g);
+        // tens of rows per tile: 32-row tiles; gate-up 64 columns (routed)
+        // or 32 (dense), down 32 columns, k split over 4 waves
+        g.slots = slots_for(g.P, g.E, 32, grouped);
+        if constexpr (EPI == EPI_GATEUP) {
+          if (grouped) {
+            g.nblk = (g.n_out + 63) / 64;
+            hipLaunchKernelGGL((stream_kernel<EPI, 2, 4, 4, 2>), dim3(grid_for(g)), dim3(256), 0,
+                               s, g);
+          } else {
+            g.nblk = (g.n_out + 31) / 32;
+            hipLaunchKernelGGL((stream_kernel<EPI, 2, 2, 4, 4>), dim3(grid_for(g)), dim3(256), 0,
+                               s, g);
+          }
+        } else {
+          g.nblk = (g.n_out + 31) / 32;
+          hipLaunchKernelGGL((stream_kernel<EPI, 2, 2, 4, 2>), dim3(grid_for(g)), dim3(256), 0, s,
+                             g);
+        }
       }
-    }
-  } else {
-    // many rows per expert. Gate-up: 256 x 256 tiles on 8 waves with the
-    // direct-to-LDS ring; with a few row tiles per expert (prefill) the
-    // blocks are numbered expert by expert in groups of 4 row tiles, so a
-    // weight tile is reused across them. Down: 128 x 128 register-staged
-    // tiles, plain order, 4 workgroups per CU. Chosen by measurement at the
-    // prefill (256 rows per expert) and skewed (up to 8191) workloads.
-    if constexpr (EPI == EPI_GATEUP) {
+    } else if constexpr (EPI == EPI_GATEUP) {
+      // 256 x 256 tiles on 8 waves with the direct-to-LDS ring; with a few row
+      // tiles per expert (prefill) the blocks are numbered expert by expert in
+      // groups of 4 row tiles so a weight tile is reused across them
       constexpr int BM = 256, BN = 256;
       g.nblk = (g.n_out + BN / 2 - 1) / (BN / 2);
       g.slots = slots_for(g.P, g.E, BM, grouped);
@@ -941,14 +961,14 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
         hipLaunchKernelGGL((tiled_dma_kernel<EPI, BM, BN, 2, 4, 2, 0, false>),
                            dim3(grid_tiled(g, false)), dim3(512), 0, s, g);
     } else {
+      // down: 128 x 128 register-staged tiles, 4 workgroups per CU
       constexpr int BM = 128, BN = 128;
       g.nblk = (g.n_out + BN - 1) / BN;
       g.slots = slots_for(g.P, g.E, BM, grouped);
       hipLaunchKernelGGL((tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 4, 0, false>),
                          dim3(grid_tiled(g, false)), dim3(256), 0, s, g);
     }
-  }
-  return hipGetLastError();
+    return hipGetLastError();
   }
 }
 

@@ -84,6 +84,29 @@ def test_gemms_bit_exact_on_exact_arithmetic(gpu_lib, T, H, E, K, I, skew):
     assert_bits_equal(bits(eo0), O.down_proj(a2, wd, sp, off, None), "expert_out unweighted")
 
 
+@pytest.mark.parametrize("skew", [False, True])
+def test_tiled_gemms_bit_exact_on_exact_arithmetic(gpu_lib, skew):
+    """Large enough for the LDS-tiled kernels (256-row gate-up tiles with the
+    direct-to-LDS ring, 128-row down tiles): 16384 pairs over 16 experts, with
+    k tails (H = 520, I = 1000 are not multiples of 64) and a column tail."""
+    T, H, E, K, I = 4096, 520, 16, 4, 1000
+    print(f"exact tiled gemm T={T} H={H} E={E} K={K} I={I} skew={skew}", flush=True)
+    seed = 77 + int(skew)
+    x = _exact_bf16(seed, (T, H), -4, 4, 1.0)
+    wgu = _exact_bf16(seed + 1, (E, 2 * I, H), -4, 4, 2.0 ** -6)
+    ids, w, off, sp = _routing_for(T, E, K, seed + 2, skew)
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), to_dev_bf16(wgu), to_dev(sp),
+                                               to_dev(off), K)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(act), O.gateup_silu(x, wgu, sp, off, K), "act")
+    a2 = _exact_bf16(seed + 3, (T * K, I), -8, 8, 2.0 ** -4)
+    wd = _exact_bf16(seed + 4, (E, H, I), -4, 4, 2.0 ** -5)
+    eo = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), to_dev_bf16(wd), to_dev(sp), to_dev(off),
+                                       to_dev(w.reshape(-1)))
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(eo), O.down_proj(a2, wd, sp, off, w.reshape(-1)), "expert_out")
+
+
 @pytest.mark.parametrize("T,H,I", [(16, 64, 32), (512, 264, 72), (40, 128, 512)])
 def test_identity_rows_bit_exact(gpu_lib, T, H, I):
     """NULL sorted_pairs/offsets: a dense expert (the shared expert)."""
