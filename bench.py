@@ -50,24 +50,37 @@ def algorithmic_work(cfg, offsets):
     return gu, dn, touched
 
 
+def kernel_code_fingerprint():
+    """sha256 of the GEMM kernel code (gemm.hip and device_math.h) with
+    comments and whitespace removed: it changes when the code changes, not
+    when a comment does."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "device_math.h"):
+        txt = open(os.path.join(ROOT, "mixture_experts_ffn_expert_amd", "csrc", name)).read()
+        txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+        txt = re.sub(r"//[^\n]*", " ", txt)
+        h.update(re.sub(r"\s+", "", txt).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(workload):
     """HBM bytes per gate-up launch from the committed rocprofv3 counter runs.
 
-    Only valid while the GEMM source is the one the counters were taken on
-    (its sha256 is recorded in the summary); otherwise None.
+    Only valid while the GEMM kernel code is the one the counters were taken
+    on (its fingerprint is recorded in the summary); otherwise None.
     """
-    import hashlib
     import re
     if workload != 2:
         return None
     summary = os.path.join(ROOT, "profiles", "decode_gateup_hbm_traffic.md")
-    src = os.path.join(ROOT, "mixture_experts_ffn_expert_amd", "csrc", "gemm.hip")
     try:
         txt = open(summary).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = kernel_code_fingerprint()
     except OSError:
         return None
-    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", txt)
+    m_sha = re.search(r"kernel_code_sha256:\s*([0-9a-f]{64})", txt)
     m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", txt)
     if not m_sha or not m_val or m_sha.group(1) != sha:
         return None

@@ -20,18 +20,22 @@
 // ceil(P/BM) + min(E, P) on the number of slots; surplus workgroups leave at
 // once.
 //
-// Two kernel shapes:
-//  * stream_kernel (few rows per expert, e.g. decode): a workgroup owns a 16-
-//    or 32-row block of one expert and 16 or 32 output columns; its 4 waves
-//    split the k range. Each weight element is used by exactly one wave, so
-//    weights go straight from HBM into MFMA operand registers
-//    (v_mfma_f32_16x16x32_bf16) with no LDS staging and no barrier in the k
-//    loop; the partial tiles meet once in LDS, added in a fixed order. The
-//    small work units keep every CU streaming to the end. HBM-bound by design.
-//  * tiled_kernel (hundreds of rows per expert, prefill): 128 x 128 block
+// Three kernel shapes, picked on the host by rows per expert and tile count:
+//  * stream_kernel (few rows per expert: decode, many small experts, a dense
+//    shared expert of a few hundred rows): a workgroup owns a 16- or 32-row
+//    block of one expert and 16..64 output columns; its waves split the k
+//    range. Each weight element is used by exactly one wave, so weights go
+//    straight from HBM into MFMA operand registers (v_mfma_f32_16x16x32_bf16)
+//    with no LDS staging and no barrier in the k loop; the partial tiles meet
+//    once in LDS, added in a fixed order. The small work units keep every CU
+//    streaming to the end. HBM-bound by design.
+//  * tiled_dma_kernel (gate-up with hundreds of rows per expert): 256 x 256
+//    block tile on 8 waves, k step 64, a 2-stage LDS ring filled by
+//    direct-to-LDS buffer loads, XOR-swizzled rows, v_mfma_f32_32x32x16_bf16.
+//  * tiled_kernel (down with hundreds of rows per expert): 128 x 128 block
 //    tile, 4 waves of 64 x 64, k step 64 staged through LDS with padded rows
 //    (conflict-free 16-byte reads), register prefetch of the next k step
-//    during the MFMAs (v_mfma_f32_32x32x16_bf16).
+//    during the MFMAs, 4 workgroups per CU.
 //
 // Epilogues (all per element, f32, no contraction):
 //  * gate-up: the block loads the gate rows [n, n+16) / [n, n+32) and the
