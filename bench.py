@@ -8,9 +8,13 @@ weights of the workload's shape) are resident in HBM before timing starts.
 
 Prints ONE JSON line. `value` is layer tokens/s (T * steps / elapsed). The
 `roofline` object describes the dominant kernel (the grouped gate-up GEMM),
-timed with HIP events on the stream it runs on, on every fifth step of the
-timed region; `cpu_baseline` times the CPU oracle on a bounded sample of the
-workload.
+timed on every step of the timed region by HIP events that its kernel
+records itself (start and end of the kernel, on the stream it runs on); `cpu_baseline` times the CPU oracle on a bounded sample of the
+workload. The steps cycle through `--layers` weight sets (same values,
+distinct addresses), so no step finds its weights in the last-level cache
+left by the step before, as in a model whose consecutive MoE layers hold
+distinct weights. `hipgraph` times the same steps captured once into a HIP
+graph and replayed.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
        (--workload picks one of the five workloads, default 2: the 32-token
@@ -114,6 +118,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=2,
+                    help="distinct weight sets (layers) the steps cycle through, so that no "
+                         "step finds its weights in the 256 MB last-level cache (default 2)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the hipGraph-replay timing of the same steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM byte-counter calibration)")
     args = ap.parse_args()
@@ -149,11 +158,14 @@ def main():
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
 
-    x, w_r, w_gu, w_d = bf(d["x"]), bf(d["w_r"]), bf(d["w_gu"]), bf(d["w_d"])
+    x = bf(d["x"])
     bias = torch.from_numpy(d["router_bias"]).to(dev) if "router_bias" in d else None
-    w_gu_s = bf(d["w_gu_s"]) if "w_gu_s" in d else None
-    w_d_s = bf(d["w_d_s"]) if "w_d_s" in d else None
-    w_g = bf(d["w_g"]) if "w_g" in d else None
+    # one weight set per layer: the same values at distinct addresses, as
+    # consecutive MoE layers of a model hold distinct weights
+    names = [n for n in ("w_r", "w_gu", "w_d", "w_gu_s", "w_d_s", "w_g") if n in d]
+    first = {n: bf(d[n]) for n in names}
+    layers = [first] + [{n: t.clone() for n, t in first.items()}
+                        for _ in range(max(1, args.layers) - 1)]
     T, H, E, K, I = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I
     bufs = {}
     ws_bytes = moe.moe_route_workspace_bytes(T, E, K)
@@ -161,29 +173,32 @@ def main():
     stream = torch.cuda.current_stream()
     ev = []
 
-    # HIP events bracket the two grouped GEMMs on every EVENT_EVERY-th timed
-    # step: recording an event costs a ~6 us gap in the queue, so bracketing
-    # every step would inflate the step time it is measured in.
-    EVENT_EVERY = 5
+    def new_event():
+        # recorded once here so that the HIP event exists before a kernel
+        # records into it
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
 
-    def step(record):
+    def step(record, lw):
+        w_r, w_gu, w_d = lw["w_r"], lw["w_gu"], lw["w_d"]
+        w_gu_s, w_d_s, w_g = lw.get("w_gu_s"), lw.get("w_d_s"), lw.get("w_g")
         logits = moe.moe_router_logits(x, w_r, bias, bufs.get("logits"))
         bufs["logits"] = logits
         ids, w, off, sp = moe.moe_route(logits, K, bufs.get("ids"), bufs.get("w"),
                                         bufs.get("offsets"), bufs.get("sorted"), ws)
         bufs.update(ids=ids, w=w, offsets=off, sorted=sp)
         if record:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            # the GEMM kernels record their own start and end (no packets
+            # added to the queue), on the stream they run on
+            evs = record
+            moe.moe_time_next_gemm(evs[0], evs[1])
         act = moe.moe_grouped_gemm_gateup_silu(x, w_gu, sp, off, K, bufs.get("act"))
         if record:
-            e1 = torch.cuda.Event(enable_timing=True)
-            e1.record(stream)
+            moe.moe_time_next_gemm(evs[2], evs[3])
         eo = moe.moe_grouped_gemm_down(act, w_d, sp, off, w, bufs.get("expert_out"))
         if record:
-            e2 = torch.cuda.Event(enable_timing=True)
-            e2.record(stream)
-            ev.append((e0, e1, e2))
+            ev.append(evs)
         bufs.update(act=act, expert_out=eo)
         sd = gl = None
         if w_gu_s is not None:
@@ -197,17 +212,40 @@ def main():
         out = moe.moe_combine_gate(eo, T, K, None, 1.0, sd, gl, bufs.get("out"))
         bufs["out"] = out
 
-    for _ in range(args.warmup):
-        step(False)
+    L = len(layers)
+    for i in range(max(args.warmup, L)):
+        step(False, layers[i % L])
+    pool = [[new_event() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i % EVENT_EVERY == 0)
+        step(pool[i], layers[i % L])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    gu_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    dn_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    graph = None
+    if not args.no_graph:
+        # the same steps captured once (one per layer) and replayed: no host
+        # launch work between kernels; every buffer already exists, so the
+        # capture allocates nothing
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(L):
+                step(False, layers[i])
+        reps = max(1, args.steps // L)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        g_elapsed = time.perf_counter() - t1
+        graph = {"steps": reps * L, "ms_per_step": g_elapsed / (reps * L) * 1e3,
+                 "tokens_per_s": T * reps * L / g_elapsed}
+
+    gu_ms = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev]))
+    dn_ms = float(np.mean([c.elapsed_time(d_) for _, _, c, d_ in ev]))
     offsets = bufs["offsets"].cpu().numpy()
     gu, dn, touched = algorithmic_work(cfg, offsets)
     hbm_bound = (gu["flops"] / gu["bytes"]) < (MFMA_BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
@@ -251,6 +289,8 @@ def main():
             "algorithmic_gbs": gemm_bytes / (gemm_ms * 1e-3) / 1e9,
             "gbs_frac_of_hbm_peak": gemm_bytes / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
+        "hipgraph": graph,
+        "weight_sets": L,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

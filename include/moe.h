@@ -84,6 +84,16 @@ const char* moe_last_error(void);
  * first use. Returns MOE_E_HIP (with a message) on another architecture. */
 moe_status moe_init(void);
 
+/* Measurement only. Arms kernel timing for the next GEMM call
+ * (moe_router_logits, moe_grouped_gemm_gateup_silu or moe_grouped_gemm_down)
+ * made by this host thread: its kernel is launched so that it records its
+ * own start and end into `start` and `stop` (hipEvent_t created by the
+ * caller), and hipEventElapsedTime(start, stop) then gives the kernel's
+ * duration without the launch gap. The next GEMM call disarms it whether or
+ * not it launches (T = 0, a refused argument). Both NULL disarms; one NULL
+ * is MOE_E_INVALID. Not for use under hipGraph capture. */
+moe_status moe_time_next_gemm(void* start, void* stop);
+
 /*
  * Router / gate logits helper (not a contract step; the router itself is the
  * ungrouped softmax top-k of [PR 509] Honest gaps).

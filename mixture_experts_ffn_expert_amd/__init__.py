@@ -13,7 +13,8 @@ Functions (same names as the C ABI):
   moe_grouped_gemm_down(act, w_d, sorted_pairs, expert_offsets, pair_w, expert_out=None)
   moe_combine_gate(expert_out, T, K, topk_w=None, routed_scale=1.0, shared=None,
                    gate_logit=None, out=None, out_dtype=torch.bfloat16)
-plus ``moe_layer`` which enqueues one whole layer.
+plus ``moe_layer`` which enqueues one whole layer, and the measurement-only
+  moe_time_next_gemm(start, stop)   (torch.cuda.Event pair, or None, None)
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ import os
 __all__ = [
     "MoeError", "load", "lib_path", "moe_init", "moe_router_logits", "moe_route",
     "moe_route_workspace_bytes", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
-    "moe_combine_gate", "moe_layer", "MOE_F32", "MOE_BF16", "MOE_F16", "SYMBOLS",
+    "moe_combine_gate", "moe_layer", "moe_time_next_gemm", "MOE_F32", "MOE_BF16", "MOE_F16", "SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +41,7 @@ _st = ctypes.c_int
 SYMBOLS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_init": (_st, []),
+    "moe_time_next_gemm": (_st, [_p, _p]),
     "moe_router_logits": (_st, [_p, _i, _i, _p, _i, _p, _p, _p]),
     "moe_route_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
     "moe_route": (_st, [_p, _i, _i, _i, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
@@ -123,6 +125,22 @@ def _dt_code(dtype):
 
 def moe_init():
     _check(load().moe_init())
+
+
+def moe_time_next_gemm(start=None, stop=None):
+    """Measurement only: the next GEMM call made by this thread records its
+    kernel's own start and end into ``start`` and ``stop``
+    (``torch.cuda.Event(enable_timing=True)``, each recorded once beforehand
+    so that the HIP event exists). ``None, None`` disarms."""
+    def handle(ev, name):
+        if ev is None:
+            return None
+        h = int(ev.cuda_event)
+        if h == 0:
+            raise MoeError(1, f"moe_time_next_gemm: {name} event was never recorded, so it does "
+                              f"not exist yet")
+        return ctypes.c_void_p(h)
+    _check(load().moe_time_next_gemm(handle(start, "start"), handle(stop, "stop")))
 
 
 def moe_router_logits(x, w, bias=None, out=None, stream=None):

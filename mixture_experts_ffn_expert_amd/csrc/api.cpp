@@ -102,6 +102,12 @@ bool fits_i32(long long v) { return v >= 0 && v < (1LL << 31); }
 // block) through a buffer resource of at most 2^31 bytes: 2^30 bf16 values.
 bool fits_buf(long long elems) { return elems >= 0 && elems < (1LL << 30); }
 
+// Timing armed by moe_time_next_gemm applies to one GEMM call only: every
+// GEMM entry point disarms it on return, whether or not it launched.
+struct DisarmTiming {
+  ~DisarmTiming() { moe::set_gemm_timing(nullptr, nullptr); }
+};
+
 }  // namespace
 
 extern "C" {
@@ -113,9 +119,18 @@ moe_status moe_init(void) {
   return check_device("moe_init");
 }
 
+moe_status moe_time_next_gemm(void* start, void* stop) {
+  clear_err();
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(MOE_E_INVALID, "moe_time_next_gemm: start and stop must both be set or both NULL");
+  moe::set_gemm_timing(static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
+  return MOE_OK;
+}
+
 moe_status moe_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
                              const float* bias, float* out, moe_stream_t stream) {
   const char* fn = "moe_router_logits";
+  DisarmTiming disarm;
   clear_err();
   if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
   if (H <= 0 || H % 8) return fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);
@@ -171,6 +186,7 @@ moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const u
                                         const int32_t* expert_offsets, int K, uint16_t* act,
                                         moe_stream_t stream) {
   const char* fn = "moe_grouped_gemm_gateup_silu";
+  DisarmTiming disarm;
   clear_err();
   if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
   if (H <= 0 || H % 8) return fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);
@@ -203,6 +219,7 @@ moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const uint16
                                  const int32_t* expert_offsets, const float* pair_w,
                                  uint16_t* expert_out, moe_stream_t stream) {
   const char* fn = "moe_grouped_gemm_down";
+  DisarmTiming disarm;
   clear_err();
   if (P < 0) return fail(MOE_E_SHAPE, "%s: P=%d is negative", fn, P);
   if (H <= 0 || H % 8) return fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);

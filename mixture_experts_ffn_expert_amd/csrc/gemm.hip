@@ -43,6 +43,8 @@
 //    gate and up of the same (row, column): act = bf16(silu(bf16(g)) * bf16(u)).
 //  * down: bf16(acc * pair_w[p]) stored at pair row p = sorted[q].
 //  * f32: acc (+ bias) stored as f32 (router and gate logits).
+#include <hip/hip_ext.h>
+
 #include "device_math.h"
 #include "launch.h"
 
@@ -637,10 +639,11 @@ __device__ __forceinline__ i32x4_t raw_rsrc(const void* base, uint32_t bytes) {
 }
 
 __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  // M0 is an input operand: the compiler places the LDS address there itself
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+               : "memory");
 }
 
 // Wait until at most N of this wave's vector loads are in flight and all its
@@ -892,6 +895,31 @@ static inline unsigned grid_for(const GemmArgs& g) {
   return (unsigned)((long long)g.slots * g.nblk);
 }
 
+// Optional kernel timing, armed per host thread by set_gemm_timing: the next
+// GEMM launch goes through hipExtLaunchKernel, which records the kernel's own
+// start and end into the two events (no extra packets in the queue), and
+// disarms it.
+static thread_local hipEvent_t t_start = nullptr;
+static thread_local hipEvent_t t_stop = nullptr;
+
+void set_gemm_timing(hipEvent_t start, hipEvent_t stop) {
+  t_start = start;
+  t_stop = stop;
+}
+
+template <typename Kernel>
+static hipError_t run(Kernel kernel, unsigned grid, unsigned block, hipStream_t s, GemmArgs& g) {
+  if (t_start != nullptr && t_stop != nullptr) {
+    const hipEvent_t a = t_start, b = t_stop;
+    t_start = t_stop = nullptr;
+    void* args[] = {&g};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block), args,
+                              0, s, a, b, 0);
+  }
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, s, g);
+  return hipGetLastError();
+}
+
 // Kernel shapes were chosen by measurement on MI355X at the five workload
 // shapes (decode 32 tokens / 128 experts, prefill 4096 tokens, 256 experts with
 // 16 rows each, a 512-row dense shared expert, skewed 8192 tokens).
@@ -904,52 +932,43 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
       // a few tokens: 16 rows x 16 columns per workgroup, k split over 8 waves
       g.nblk = (g.n_out + 15) / 16;
       g.slots = slots_for(g.P, g.E, 16, false);
-      hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 8, 4>), dim3(grid_for(g)), dim3(512), 0, s, g);
-    } else {
-      // many tokens: 32 rows x 64 columns, k split over 4 waves
-      g.nblk = (g.n_out + 63) / 64;
-      g.slots = slots_for(g.P, g.E, 32, false);
-      hipLaunchKernelGGL((stream_kernel<EPI, 2, 4, 4, 2>), dim3(grid_for(g)), dim3(256), 0, s, g);
+      return run(stream_kernel<EPI, 1, 1, 8, 4>, grid_for(g), 512, s, g);
     }
-    return hipGetLastError();
+    // many tokens: 32 rows x 64 columns, k split over 4 waves
+    g.nblk = (g.n_out + 63) / 64;
+    g.slots = slots_for(g.P, g.E, 32, false);
+    return run(stream_kernel<EPI, 2, 4, 4, 2>, grid_for(g), 256, s, g);
   } else {
     const double avg_rows = grouped ? (double)g.P / (double)g.E : (double)g.P;
     // LDS tiles pay off with hundreds of rows per expert and enough tiles to
     // occupy the chip; everything else streams the weights.
     const int tbm = (EPI == EPI_GATEUP) ? 256 : 128;
-    const int tcols = (EPI == EPI_GATEUP) ? 128 : 128;
-    const long long tiled_blocks = (long long)(g.P / tbm) * ((g.n_out + tcols - 1) / tcols);
+    const long long tiled_blocks = (long long)(g.P / tbm) * ((g.n_out + 127) / 128);
     if (avg_rows <= 24.0 || tiled_blocks < 512) {
       if (avg_rows <= 8.0) {
-        // decode-like: 16-row tiles; gate-up 16 columns (gate + up fragments)
-        // with k split over 4 waves, down 16 columns with k split over 2
+        // decode-like: 16-row tiles of 16 columns; gate-up (gate + up
+        // fragments) splits k over 4 waves with 8 k steps in flight per
+        // wave, down splits k over 3 waves with 2 in flight
         g.slots = slots_for(g.P, g.E, 16, grouped);
         g.nblk = (g.n_out + 15) / 16;
         if constexpr (EPI == EPI_GATEUP)
-          hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 4, 4>), dim3(grid_for(g)), dim3(256), 0, s,
-                             g);
+          return run(stream_kernel<EPI, 1, 1, 4, 8>, grid_for(g), 256, s, g);
         else
-          hipLaunchKernelGGL((stream_kernel<EPI, 1, 1, 2, 4>), dim3(grid_for(g)), dim3(128), 0, s,
-                             g);
-      } else {
-        // tens of rows per tile: 32-row tiles; gate-up 64 columns (routed)
-        // or 32 (dense), down 32 columns, k split over 4 waves
-        g.slots = slots_for(g.P, g.E, 32, grouped);
-        if constexpr (EPI == EPI_GATEUP) {
-          if (grouped) {
-            g.nblk = (g.n_out + 63) / 64;
-            hipLaunchKernelGGL((stream_kernel<EPI, 2, 4, 4, 2>), dim3(grid_for(g)), dim3(256), 0,
-                               s, g);
-          } else {
-            g.nblk = (g.n_out + 31) / 32;
-            hipLaunchKernelGGL((stream_kernel<EPI, 2, 2, 4, 4>), dim3(grid_for(g)), dim3(256), 0,
-                               s, g);
-          }
-        } else {
-          g.nblk = (g.n_out + 31) / 32;
-          hipLaunchKernelGGL((stream_kernel<EPI, 2, 2, 4, 2>), dim3(grid_for(g)), dim3(256), 0, s,
-                             g);
+          return run(stream_kernel<EPI, 1, 1, 3, 2>, grid_for(g), 192, s, g);
+      }
+      // tens of rows per tile: 32-row tiles; gate-up 64 columns (routed)
+      // or 32 (dense), down 32 columns, k split over 4 waves
+      g.slots = slots_for(g.P, g.E, 32, grouped);
+      if constexpr (EPI == EPI_GATEUP) {
+        if (grouped) {
+          g.nblk = (g.n_out + 63) / 64;
+          return run(stream_kernel<EPI, 2, 4, 4, 2>, grid_for(g), 256, s, g);
         }
+        g.nblk = (g.n_out + 31) / 32;
+        return run(stream_kernel<EPI, 2, 2, 4, 4>, grid_for(g), 256, s, g);
+      } else {
+        g.nblk = (g.n_out + 31) / 32;
+        return run(stream_kernel<EPI, 2, 2, 4, 2>, grid_for(g), 256, s, g);
       }
     } else if constexpr (EPI == EPI_GATEUP) {
       // 256 x 256 tiles on 8 waves with the direct-to-LDS ring; with a few row
@@ -959,20 +978,17 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
       g.nblk = (g.n_out + BN / 2 - 1) / (BN / 2);
       g.slots = slots_for(g.P, g.E, BM, grouped);
       if (avg_rows <= 384.0)
-        hipLaunchKernelGGL((tiled_dma_kernel<EPI, BM, BN, 2, 4, 2, 4, false>),
-                           dim3(grid_tiled(g, false)), dim3(512), 0, s, g);
-      else
-        hipLaunchKernelGGL((tiled_dma_kernel<EPI, BM, BN, 2, 4, 2, 0, false>),
-                           dim3(grid_tiled(g, false)), dim3(512), 0, s, g);
+        return run(tiled_dma_kernel<EPI, BM, BN, 2, 4, 2, 4, false>, grid_tiled(g, false), 512, s,
+                   g);
+      return run(tiled_dma_kernel<EPI, BM, BN, 2, 4, 2, 0, false>, grid_tiled(g, false), 512, s, g);
     } else {
       // down: 128 x 128 register-staged tiles, 4 workgroups per CU
       constexpr int BM = 128, BN = 128;
       g.nblk = (g.n_out + BN - 1) / BN;
       g.slots = slots_for(g.P, g.E, BM, grouped);
-      hipLaunchKernelGGL((tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 4, 0, false>),
-                         dim3(grid_tiled(g, false)), dim3(256), 0, s, g);
+      return run(tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 4, 0, false>, grid_tiled(g, false), 256, s,
+                 g);
     }
-    return hipGetLastError();
   }
 }
 

@@ -19,6 +19,9 @@ hipError_t launch_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w
 hipError_t launch_down(const uint16_t* act, int P, int I, const uint16_t* w_d, int E, int H,
                        const int32_t* sorted, const int32_t* offsets, const float* pair_w,
                        uint16_t* expert_out, hipStream_t s);
+// Arms kernel timing for the next GEMM launch on this host thread (both null:
+// disarm).
+void set_gemm_timing(hipEvent_t start, hipEvent_t stop);
 hipError_t launch_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
                          const float* bias, float* out, hipStream_t s);
 

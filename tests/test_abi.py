@@ -161,3 +161,17 @@ def test_product_code_never_imports_the_oracle():
                 txt = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, fn
                 assert "moe_oracle" not in txt, fn
+
+
+def test_time_next_gemm_pairs(lib):
+    assert lib.moe_time_next_gemm(A, None) == 1 and "both" in _err(lib)
+    assert lib.moe_time_next_gemm(None, A) == 1
+    assert lib.moe_time_next_gemm(None, None) == 0 and _err(lib) == ""
+
+
+def test_refused_gemm_call_disarms_timing(lib):
+    # armed with dummy handles: a refused GEMM call must disarm, so the next
+    # valid call never touches them (here the next call is refused too)
+    assert lib.moe_time_next_gemm(A, A2) == 0
+    assert lib.moe_grouped_gemm_down(A, 8, 16, A, 8, 20, A, A, None, A, None) == 3
+    assert lib.moe_router_logits(None, 0, 16, None, 8, None, None, None) == 0

@@ -243,3 +243,35 @@ def test_gemm_output_canaries(gpu_lib):
     torch.cuda.synchronize()
     assert torch.all(full[T * K * I:] == 0x7BCD).item(), "gate-up wrote past act"
     assert_bits_equal(bits(act), O.gateup_silu(x, wgu, sp, off, K), "act")
+
+
+def test_timed_gemm_launch_matches_untimed(gpu_lib):
+    """moe_time_next_gemm: the timed launch computes the same bits, the events
+    hold a positive kernel duration, and the arming covers one call only."""
+    T, H, E, K, I = 32, 2048, 128, 8, 768
+    x = W.random_bf16(11, (T, H))
+    wgu = W.random_bf16(12, (E, 2 * I, H), 1.0 / np.sqrt(H))
+    wd = W.random_bf16(13, (E, H, I), 1.0 / np.sqrt(I))
+    ids, w, off, sp = _routing_for(T, E, K, 14)
+    x_d, wgu_d, wd_d, sp_d, off_d = (to_dev_bf16(x), to_dev_bf16(wgu), to_dev_bf16(wd),
+                                     to_dev(sp), to_dev(off))
+    pw = to_dev(w.reshape(-1))
+    ref_act = gpu_lib.moe_grouped_gemm_gateup_silu(x_d, wgu_d, sp_d, off_d, K)
+    ref_eo = gpu_lib.moe_grouped_gemm_down(ref_act, wd_d, sp_d, off_d, pw)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    gpu_lib.moe_time_next_gemm(evs[0], evs[1])
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(x_d, wgu_d, sp_d, off_d, K)
+    gpu_lib.moe_time_next_gemm(evs[2], evs[3])
+    eo = gpu_lib.moe_grouped_gemm_down(act, wd_d, sp_d, off_d, pw)
+    # not armed any more: a plain launch
+    eo2 = gpu_lib.moe_grouped_gemm_down(act, wd_d, sp_d, off_d, pw)
+    torch.cuda.synchronize()
+    assert torch.equal(act.view(torch.int16), ref_act.view(torch.int16))
+    assert torch.equal(eo.view(torch.int16), ref_eo.view(torch.int16))
+    assert torch.equal(eo2.view(torch.int16), ref_eo.view(torch.int16))
+    t_gu = evs[0].elapsed_time(evs[1])
+    t_dn = evs[2].elapsed_time(evs[3])
+    assert 0.0 < t_gu < 100.0 and 0.0 < t_dn < 100.0, (t_gu, t_dn)
