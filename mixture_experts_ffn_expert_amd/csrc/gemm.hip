@@ -188,8 +188,6 @@ __device__ __forceinline__ bool find_block(const GemmArgs& g, int BM, int GM, in
   return false;
 }
 
-constexpr int kXcds = 8;
-
 // Epilogue of one output element (row q of the problem, column c).
 template <int EPI>
 __device__ __forceinline__ void store_plain(const GemmArgs& g, int q, int c, float acc) {
@@ -382,8 +380,7 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(GemmArgs g) {
 // 16-byte fragment reads). The next k step is loaded into registers while
 // the current one is multiplied (v_mfma_f32_32x32x16_bf16).
 // ---------------------------------------------------------------------------
-template <int EPI, int BM, int BN, int BK, int WM, int WN, int PF = 1, int MINB = 1, int GM = 0,
-          bool XCD = false>
+template <int EPI, int BM, int BN, int BK, int WM, int WN, int PF = 1, int MINB = 1, int GM = 0>
 __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
   constexpr int NT = 64 * WM * WN;             // threads
   constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
@@ -411,11 +408,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  int L = blockIdx.x;
-  if (XCD) {  // each XCD (every 8th workgroup, own L2) takes a contiguous run
-    const int per = gridDim.x / kXcds;
-    L = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  }
+  const int L = blockIdx.x;
   if (wave == 0) {
     int e = 0, row0 = 0, rows = 0, nb = 0;
     bool ok;
@@ -614,12 +607,16 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
 
 // ---------------------------------------------------------------------------
 // tiled_dma_kernel: BM x BN block tile (BN weight rows), WM x WN waves, k step
-// 64, NS-stage LDS ring filled by direct-to-LDS buffer loads
+// BK (64 or 32), two-slot LDS ring filled by direct-to-LDS buffer loads
 // (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at M0 + 16*l; an
-// out-of-range offset writes zeros). Stage s+NS-1 is loading while stage s is
-// multiplied, with no register staging. LDS rows are 128 bytes, unpadded;
-// 16-byte chunk c of tile row r sits in slot c ^ ((r >> 1) & 7), which keeps
-// the 16-byte fragment reads of 16 consecutive rows on distinct banks.
+// out-of-range offset writes zeros). Stage s+1 is loading while stage s is
+// multiplied, with no register staging; the MFMA operands of the next 16-wide
+// k step are read from LDS while the current step's MFMAs run, and the one
+// barrier per stage sits before the last k step of the stage, so the reads of
+// the next stage's first step overlap that step's MFMAs. LDS rows are 2*BK bytes,
+// unpadded; 16-byte chunk c of tile row r sits in slot c ^ ((r >> 1) & (BK/8 -
+// 1)), which keeps the 16-byte fragment reads of 8 consecutive rows on
+// distinct banks.
 //
 // The loads are issued from inline assembly and the waits are explicit
 // (s_waitcnt vmcnt(N) lgkmcnt(0); s_barrier): the compiler cannot tell which
@@ -654,24 +651,26 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-template <int EPI, int BM, int BN, int WM, int WN, int NS, int GM = 0, bool XCD = false>
+template <int EPI, int BM, int BN, int WM, int WN, int GM = 0, int BK = 64>
 __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
-  constexpr int BK = 64;
+  constexpr int NS = 2;                        // ring slots
   constexpr int NW = WM * WN;
   constexpr int NT = 64 * NW;
   constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
   constexpr int FM = TM / 32, FN = TN / 32;    // 32x32 fragments per wave
-  constexpr int ROWB = BK * 2;                 // bytes per tile row (128)
+  constexpr int ROWB = BK * 2;                 // bytes per tile row
+  constexpr int CPR = BK / 8;                  // 16-byte chunks per row
+  constexpr int RPL = 1024 / ROWB;             // rows per 1 KiB load
   constexpr int STAGE = (BM + BN) * ROWB;      // bytes per ring slot
-  constexpr int IPW = (BM + BN) / 8 / NW;      // 1 KiB loads per wave per stage
+  constexpr int IPW = (BM + BN) / RPL / NW;    // 1 KiB loads per wave per stage
   constexpr int OUT_COLS = (EPI == EPI_GATEUP) ? BN / 2 : BN;
   constexpr int CLD = OUT_COLS + 8;            // output staging row (elements)
-  static_assert(IPW * 8 * NW == BM + BN, "loads per wave");
+  static_assert(BK == 64 || BK == 32, "k step");
+  static_assert(IPW * RPL * NW == BM + BN, "loads per wave");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "swizzle period");
   static_assert(EPI != EPI_GATEUP || FN % 2 == 0, "gate-up pairs fragments");
   static_assert(EPI != EPI_F32, "logits use the streaming kernel");
   static_assert(BM * CLD * 2 <= NS * STAGE, "output staging fits the ring");
-  static_assert(NS >= 2 && NS <= 4, "ring depth");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE];
   __shared__ int row_dest[BM];
   __shared__ float row_w[BM];
@@ -680,11 +679,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave == 0) {
-    int L = blockIdx.x;
-    if (XCD) {  // each XCD (every 8th workgroup, own L2) takes a contiguous run
-      const int per = gridDim.x / kXcds;
-      L = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-    }
+    const int L = blockIdx.x;
     int e = 0, row0 = 0, rows = 0, nb = 0;
     bool ok;
     if (GM > 0) {
@@ -725,15 +720,15 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   const i32x4_t rsrc_a = raw_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
   const i32x4_t rsrc_b =
       raw_rsrc(g.B + (size_t)e * g.b_rows * g.kdim, (uint32_t)g.b_rows * (uint32_t)g.kdim * 2u);
-  // Load j of this wave fills tile rows [8*(wave*IPW + j), +8) of a ring
-  // slot: lane l writes slot (l%8) of row l/8, i.e. logical chunk
-  // (l%8) ^ swz(row).
+  // Load j of this wave fills tile rows [RPL*(wave*IPW + j), +RPL) of a ring
+  // slot: lane l writes slot (l%CPR) of row l/CPR, i.e. logical chunk
+  // (l%CPR) ^ swz(row).
   uint32_t voff[IPW];
   int chunk[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
-    const int r = (wave * IPW + j) * 8 + (lane >> 3);  // tile row (A rows, then B rows)
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int r = (wave * IPW + j) * RPL + lane / CPR;  // tile row (A rows, then B rows)
+    const int c = (lane % CPR) ^ ((r >> 1) & (CPR - 1));
     uint32_t ro;
     if (r < BM) {
       ro = (r < rows) ? a_row_off(g, row0 + r) : kOob;
@@ -761,7 +756,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
       const int blk = wave * IPW + j;  // uniform
       const uint32_t m0 = ring_base + slot * STAGE + blk * 1024;
       const uint32_t vo = (full || k0 + chunk[j] < g.kdim) ? voff[j] : kOob;
-      dma16(blk * 8 < BM ? rsrc_a : rsrc_b, m0, vo, soff);
+      dma16(blk * RPL < BM ? rsrc_a : rsrc_b, m0, vo, soff);
     }
   };
 
@@ -782,50 +777,57 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
     const int r = wm * TM + i * 32 + r32;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk)
-      aoff[i][kk] = r * ROWB + (((kk * 2 + khalf) ^ ((r >> 1) & 7)) * 16);
+      aoff[i][kk] = r * ROWB + (((kk * 2 + khalf) ^ ((r >> 1) & (CPR - 1))) * 16);
   }
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
     const int r = BM + wn * TN + f * 32 + r32;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk)
-      boff[f][kk] = r * ROWB + (((kk * 2 + khalf) ^ ((r >> 1) & 7)) * 16);
+      boff[f][kk] = r * ROWB + (((kk * 2 + khalf) ^ ((r >> 1) & (CPR - 1))) * 16);
   }
-  auto compute = [&](int slot) {
+  // MFMA operands of one 16-wide k step, double-buffered across steps
+  constexpr int KK = BK / 16;
+  bf16x8_t fa[2][FM], fb[2][FN];
+  auto read_step = [&](int buf, int slot, int kk) {
     const unsigned char* sb = ring + slot * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t a[FM], b[FN];
+    for (int i = 0; i < FM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(sb + aoff[i][kk]);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(sb + aoff[i][kk]);
+    for (int f = 0; f < FN; ++f) fb[buf][f] = *reinterpret_cast<const bf16x8_t*>(sb + boff[f][kk]);
+  };
+  auto mfma_step = [&](int buf) {
 #pragma unroll
-      for (int f = 0; f < FN; ++f) b[f] = *reinterpret_cast<const bf16x8_t*>(sb + boff[f][kk]);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int f = 0; f < FN; ++f)
-          acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
-    }
+      for (int f = 0; f < FN; ++f)
+        acc[i][f] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][f], acc[i][f], 0, 0, 0);
   };
 
   const int nk = (g.kdim + BK - 1) / BK;
   __syncthreads();  // row tables written; ring free
-#pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) issue(st, st * BK);
+  issue(0, 0);
+  wait_barrier<0>();  // stage 0 landed (every wave's loads)
+  if (nk > 1) issue(1, BK);
+  read_step(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most (stages issued after it) * IPW of
-    // this wave's loads are still in flight; the barrier makes every wave's
-    // loads of stage kt visible and every wave done with stage kt - 1
-    const int after = min(NS - 2, nk - 1 - kt);
-    if (after >= 2)
-      wait_barrier<2 * IPW>();
-    else if (after == 1)
-      wait_barrier<IPW>();
-    else
-      wait_barrier<0>();
-    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, (kt + NS - 1) * BK);
-    compute(kt % NS);
+    const int cur = kt & 1;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int b = kk & 1;
+      if (kk + 1 < KK) {
+        read_step(b ^ 1, cur, kk + 1);
+      } else if (kt + 1 < nk) {
+        // Stage kt+1 has landed (this wave's loads: vmcnt(0); the others':
+        // the barrier), and every wave has finished its LDS reads of stage
+        // kt (lgkmcnt(0) before the barrier), so its slot takes stage kt+2.
+        wait_barrier<0>();
+        if (kt + 2 < nk) issue(cur, (kt + 2) * BK);
+        read_step(b ^ 1, cur ^ 1, 0);
+      }
+      mfma_step(b);
+    }
   }
   wait_barrier<0>();  // ring free for the output staging
 
@@ -877,14 +879,6 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
 static inline int slots_for(int P, int E, int BM, bool grouped) {
   const int full = (P + BM - 1) / BM;
   return grouped ? full + (E < P ? E : P) : full;
-}
-
-// Grid of the tiled kernel: slots x nblk, rounded up to a multiple of the
-// XCD count when the XCD renumbering is on.
-static inline unsigned grid_tiled(const GemmArgs& g, bool xcd) {
-  long long n = (long long)g.slots * g.nblk;
-  if (xcd) n = (n + kXcds - 1) / kXcds * kXcds;
-  return (unsigned)n;
 }
 
 // Grid of slots x nblk workgroups. Consecutive workgroups take adjacent
@@ -971,23 +965,19 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
         return run(stream_kernel<EPI, 2, 2, 4, 2>, grid_for(g), 256, s, g);
       }
     } else if constexpr (EPI == EPI_GATEUP) {
-      // 256 x 256 tiles on 8 waves with the direct-to-LDS ring; with a few row
-      // tiles per expert (prefill) the blocks are numbered expert by expert in
-      // groups of 4 row tiles so a weight tile is reused across them
+      // 256 x 256 tiles on 8 waves with the direct-to-LDS ring; blocks are
+      // numbered expert by expert in groups of 4 row tiles, so a weight tile
+      // is reused by 4 consecutive workgroups while it is in L2
       constexpr int BM = 256, BN = 256;
       g.nblk = (g.n_out + BN / 2 - 1) / (BN / 2);
       g.slots = slots_for(g.P, g.E, BM, grouped);
-      if (avg_rows <= 384.0)
-        return run(tiled_dma_kernel<EPI, BM, BN, 2, 4, 2, 4, false>, grid_tiled(g, false), 512, s,
-                   g);
-      return run(tiled_dma_kernel<EPI, BM, BN, 2, 4, 2, 0, false>, grid_tiled(g, false), 512, s, g);
+      return run(tiled_dma_kernel<EPI, BM, BN, 2, 4, 4>, grid_for(g), 512, s, g);
     } else {
       // down: 128 x 128 register-staged tiles, 4 workgroups per CU
       constexpr int BM = 128, BN = 128;
       g.nblk = (g.n_out + BN - 1) / BN;
       g.slots = slots_for(g.P, g.E, BM, grouped);
-      return run(tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 4, 0, false>, grid_tiled(g, false), 256, s,
-                 g);
+      return run(tiled_kernel<EPI, BM, BN, 64, 2, 2, 1, 4, 0>, grid_for(g), 256, s, g);
     }
   }
 }
