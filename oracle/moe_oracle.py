@@ -42,6 +42,7 @@ import numpy as np
 __all__ = [
     "bf16_from_f32", "f32_from_bf16", "pexp", "sigmoid", "silu",
     "router_logits", "topk_ids", "topk_weights", "route", "group_pairs",
+    "tree_sum64", "router_scores", "select_scored", "route_scored",
     "gateup_silu", "down_proj", "shared_expert", "gate_logit",
     "combine_gate", "moe_layer",
 ]
@@ -240,6 +241,135 @@ def route(logits, K: int):
     ids = topk_ids(logits, K)
     w = topk_weights(logits, ids)
     offsets, sorted_pairs = group_pairs(ids, np.asarray(logits).shape[1])
+    return ids, w, offsets, sorted_pairs
+
+
+# ---------------------------------------------------------------------------
+# Routing: sigmoid, biased and group-limited router forms. [Issue 3094] row
+# statement and [PR 509] Honest gaps name them only as the router gaps that
+# remain (the DeepSeek-V2 / Dots3 grouped and sigmoid forms, the grouped /
+# bias / noaux_tc forms). READING: their arithmetic is taken from the
+# published DeepSeek-V2 and DeepSeek-V3 technical reports -- affinity scores
+# by softmax or sigmoid; an optional per-expert bias that steers selection
+# only; selection limited to the top groups of consecutive experts, a group
+# scored by its best expert (V2) or by its two best experts summed (V3);
+# gate weights from the unbiased scores, optionally renormalised over the
+# chosen experts.
+# ---------------------------------------------------------------------------
+def tree_sum64(z) -> np.ndarray:
+    """f32 sum over the last axis in the order of a 64-lane butterfly.
+
+    READING (the order a full softmax sums in): element e goes to lane
+    e mod 64, each lane adds its elements in increasing e (a lane with none
+    holds +0), then for m = 32, 16, 8, 4, 2, 1 every lane l adds lane l xor m;
+    lane 0's value is the sum. Each addition is one rounded f32 add.
+    """
+    z = np.asarray(z, dtype=F32)
+    T, E = z.shape
+    p = np.zeros((T, 64), dtype=F32)
+    for lane in range(min(64, E)):
+        acc = z[:, lane].copy()
+        for e in range(lane + 64, E, 64):
+            acc = (acc + z[:, e]).astype(F32)
+        p[:, lane] = acc
+    partner = np.arange(64)
+    for m in (32, 16, 8, 4, 2, 1):
+        p = (p + p[:, partner ^ m]).astype(F32)
+    return p[:, 0].copy()
+
+
+def router_scores(logits, score: str) -> np.ndarray:
+    """Affinity scores s[t,e] of every expert, f32.
+
+    sigmoid: s = 1 / (1 + e^-l). softmax (over all E): m = max_e l,
+    z = pexp(l - m), S = tree_sum64(z), s = z / S (one correctly rounded
+    divide). A NaN logit is used as -inf, as in the selection.
+    """
+    l = np.asarray(logits, dtype=F32)
+    l = np.where(np.isnan(l), F32(-np.inf), l).astype(F32)
+    if score == "sigmoid":
+        return sigmoid(l)
+    if score != "softmax":
+        raise ValueError(f"router_scores: unknown score function {score!r}")
+    m = np.max(l, axis=1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        z = pexp((l - m).astype(F32))
+    S = tree_sum64(z)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return (z / S[:, None]).astype(F32)
+
+
+def _rounds_of_max(val, allowed, n: int) -> np.ndarray:
+    """n rounds of "take the largest remaining allowed entry, ties to the
+    lower index" over the last axis; returns the picked indices in order."""
+    T = val.shape[0]
+    taken = np.zeros(val.shape, dtype=bool)
+    out = np.empty((T, n), dtype=np.int64)
+    rows = np.arange(T)
+    for k in range(n):
+        live = allowed & ~taken
+        best = np.max(np.where(live, val, F32(-np.inf)), axis=1)
+        pick = np.argmax(live & (val == best[:, None]), axis=1)
+        out[:, k] = pick
+        taken[rows, pick] = True
+    return out
+
+
+def select_scored(scores, K: int, bias=None, n_group: int = 1, topk_group: int = 1,
+                  group_score: str = "max") -> np.ndarray:
+    """Expert ids [T, K] chosen from the scores, in selection order.
+
+    Selection value c = s (+ bias[e], one f32 add when a bias is given); NaN
+    ranks as -inf. With n_group > 1 the experts form n_group groups of
+    E / n_group consecutive ids; a group's score is its largest c ("max") or
+    the f32 sum of its two largest c ("top2"; a NaN sum ranks as -inf); the
+    topk_group best groups (ties to the lower group) stay allowed. Then K
+    rounds pick the largest allowed c, ties to the lower id.
+    """
+    s = np.asarray(scores, dtype=F32)
+    T, E = s.shape
+    c = s if bias is None else (s + np.asarray(bias, dtype=F32)[None, :]).astype(F32)
+    c = np.where(np.isnan(c), F32(-np.inf), c).astype(F32)
+    allowed = np.ones((T, E), dtype=bool)
+    if n_group > 1:
+        if E % n_group or not 1 <= topk_group <= n_group:
+            raise ValueError("select_scored: bad group shape")
+        gs = E // n_group
+        cg = c.reshape(T, n_group, gs)
+        if group_score == "max":
+            g = np.max(cg, axis=2)
+        elif group_score == "top2":
+            srt = -np.sort(-cg, axis=2)
+            g = srt[:, :, 0] if gs == 1 else (srt[:, :, 0] + srt[:, :, 1]).astype(F32)
+        else:
+            raise ValueError(f"select_scored: unknown group score {group_score!r}")
+        g = np.where(np.isnan(g), F32(-np.inf), g).astype(F32)
+        groups = _rounds_of_max(g, np.ones(g.shape, dtype=bool), topk_group)
+        gmask = np.zeros((T, n_group), dtype=bool)
+        np.put_along_axis(gmask, groups, True, axis=1)
+        allowed = np.repeat(gmask, gs, axis=1)
+        if topk_group * gs < K:
+            raise ValueError("select_scored: fewer allowed experts than K")
+    return _rounds_of_max(c, allowed, K).astype(np.int32)
+
+
+def route_scored(logits, K: int, score: str = "softmax", bias=None, n_group: int = 1,
+                 topk_group: int = 1, group_score: str = "max", renormalize: bool = True):
+    """Ids, gate weights, expert offsets and sorted pairs of the general router.
+
+    Weights are the unbiased scores of the chosen experts, w_k = s[e_k]; with
+    renormalize, w_k = s[e_k] / (((s[e_0] + s[e_1]) + ...) + s[e_{K-1}]).
+    """
+    s = router_scores(logits, score)
+    ids = select_scored(s, K, bias, n_group, topk_group, group_score)
+    w = np.take_along_axis(s, ids.astype(np.int64), axis=1).astype(F32)
+    if renormalize:
+        S = w[:, 0].copy()
+        for k in range(1, K):
+            S = (S + w[:, k]).astype(F32)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            w = (w / S[:, None]).astype(F32)
+    offsets, sorted_pairs = group_pairs(ids, s.shape[1])
     return ids, w, offsets, sorted_pairs
 
 
