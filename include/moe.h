@@ -133,6 +133,49 @@ moe_status moe_route(const float* logits, int T, int E, int K, int32_t* topk_ids
                      float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
                      void* ws, size_t ws_bytes, moe_stream_t stream);
 
+typedef enum {
+  MOE_SCORE_SOFTMAX = 0, /* softmax over all E experts */
+  MOE_SCORE_SIGMOID = 1  /* sigmoid of each logit */
+} moe_score;
+
+typedef enum {
+  MOE_GROUP_MAX = 0,     /* a group is scored by its largest selection value */
+  MOE_GROUP_TOP2_SUM = 1 /* ... by the sum of its two largest */
+} moe_group_score;
+
+/*
+ * General router: sigmoid or full-softmax scores, a selection bias and
+ * group-limited selection, then the same grouping as moe_route. These are the
+ * router forms [Issue 3094] (row statement: the DeepSeek-V2 / Dots3 grouped
+ * and sigmoid router gaps) and [PR 509] (Honest gaps: grouped / bias /
+ * noaux_tc forms) name as the gaps left; the arithmetic is read from the
+ * DeepSeek-V2 and DeepSeek-V3 technical reports. Per token, f32, each
+ * operation rounded on its own:
+ *   s_e = sigmoid(l_e)                                  (MOE_SCORE_SIGMOID)
+ *   s_e = z_e / S, z_e = exp(l_e - max_j l_j), S = sum of z in the order of a
+ *         64-lane butterfly (lane e%64 adds its z in increasing e, then lanes
+ *         l and l^m are added for m = 32, 16, 8, 4, 2, 1)  (MOE_SCORE_SOFTMAX)
+ *   c_e = s_e + selection_bias[e] (selection_bias NULL: c_e = s_e); NaN
+ *         ranks as -inf
+ *   n_group > 1: experts form n_group groups of E/n_group consecutive ids; a
+ *         group scores max c (MOE_GROUP_MAX) or the f32 sum of its two largest
+ *         c (MOE_GROUP_TOP2_SUM); the topk_group best groups (ties to the
+ *         lower group) stay allowed
+ *   topk_ids: K rounds of the largest allowed c, ties to the lower id
+ *   topk_w:   w_k = s of expert k (the bias steers selection only); with
+ *             renormalize = 1, w_k / (((w_0 + w_1) + ...) + w_{K-1})
+ * exp is the library's f32 exp (as in moe_route), the divides correctly
+ * rounded. Limits: 1 <= n_group <= 64, n_group divides E, 1 <= topk_group <=
+ * n_group, topk_group * E/n_group >= K (MOE_E_SHAPE otherwise);
+ * renormalize in {0, 1}. selection_bias is f32 [E] device memory or NULL.
+ * Outputs, workspace and the rest of the contract as moe_route.
+ */
+moe_status moe_route_scored(const float* logits, int T, int E, int K, moe_score score,
+                            const float* selection_bias, int n_group, int topk_group,
+                            moe_group_score group_score, int renormalize, int32_t* topk_ids,
+                            float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                            void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /*
  * Grouped gate-up GEMM with SiLU-mul ([Issue 3094] row statement, N1).
  * For sorted row q of expert e (p = sorted_pairs[q], token t = p / K):

@@ -9,6 +9,8 @@ there is no fallback path.
 Functions (same names as the C ABI):
   moe_router_logits(x, w, bias=None, out=None)                -> f32 [T, N]
   moe_route(logits, K, ...)                                   -> ids, w, offsets, sorted_pairs
+  moe_route_scored(logits, K, score, selection_bias, n_group, topk_group, group_score,
+                   renormalize, ...)                          -> ids, w, offsets, sorted_pairs
   moe_grouped_gemm_gateup_silu(x, w_gu, sorted_pairs, expert_offsets, K, act=None)
   moe_grouped_gemm_down(act, w_d, sorted_pairs, expert_offsets, pair_w, expert_out=None)
   moe_combine_gate(expert_out, T, K, topk_w=None, routed_scale=1.0, shared=None,
@@ -23,7 +25,7 @@ import os
 
 __all__ = [
     "MoeError", "load", "lib_path", "moe_init", "moe_router_logits", "moe_route",
-    "moe_route_workspace_bytes", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
+    "moe_route_workspace_bytes", "moe_route_scored", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
     "moe_combine_gate", "moe_layer", "moe_time_next_gemm", "MOE_F32", "MOE_BF16", "MOE_F16", "SYMBOLS",
 ]
 
@@ -45,6 +47,8 @@ SYMBOLS = {
     "moe_router_logits": (_st, [_p, _i, _i, _p, _i, _p, _p, _p]),
     "moe_route_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
     "moe_route": (_st, [_p, _i, _i, _i, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
+    "moe_route_scored": (_st, [_p, _i, _i, _i, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p,
+                               ctypes.c_size_t, _p]),
     "moe_grouped_gemm_gateup_silu": (_st, [_p, _i, _i, _p, _i, _i, _p, _p, _i, _p, _p]),
     "moe_grouped_gemm_down": (_st, [_p, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p]),
     "moe_combine_gate": (_st, [_p, _i, _i, _i, _i, _p, ctypes.c_float, _p, _i, _p, _p, _i, _p]),
@@ -189,6 +193,50 @@ def moe_route(logits, K, topk_ids=None, topk_w=None, expert_offsets=None, sorted
     _check(load().moe_route(_ptr(logits), T, E, K, _ptr(topk_ids), _ptr(topk_w),
                             _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(workspace), ws_bytes,
                             _stream(stream)))
+    return topk_ids, topk_w, expert_offsets, sorted_pairs
+
+
+MOE_SCORE = {"softmax": 0, "sigmoid": 1}
+MOE_GROUP_SCORE = {"max": 0, "top2": 1}
+
+
+def moe_route_scored(logits, K, score="softmax", selection_bias=None, n_group=1, topk_group=1,
+                     group_score="max", renormalize=True, topk_ids=None, topk_w=None,
+                     expert_offsets=None, sorted_pairs=None, workspace=None, stream=None):
+    """General router (sigmoid / full-softmax scores, selection bias,
+    group-limited selection); outputs as ``moe_route``."""
+    import torch
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    if score not in MOE_SCORE:
+        raise MoeError(1, f"score must be one of {sorted(MOE_SCORE)}, got {score!r}")
+    if group_score not in MOE_GROUP_SCORE:
+        raise MoeError(1, f"group_score must be one of {sorted(MOE_GROUP_SCORE)}, "
+                          f"got {group_score!r}")
+    if selection_bias is not None:
+        _need(selection_bias, "selection_bias", torch.float32, shape=(E,))
+    dev = logits.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if expert_offsets is None:
+        expert_offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    if sorted_pairs is None:
+        sorted_pairs = torch.empty((T * K,), dtype=torch.int32, device=dev)
+    _need(topk_ids, "topk_ids", torch.int32, shape=(T, K))
+    _need(topk_w, "topk_w", torch.float32, shape=(T, K))
+    _need(expert_offsets, "expert_offsets", torch.int32, shape=(E + 1,))
+    _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * K,))
+    need = moe_route_workspace_bytes(T, E, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().moe_route_scored(
+        _ptr(logits), T, E, K, MOE_SCORE[score], _ptr(selection_bias), int(n_group),
+        int(topk_group), MOE_GROUP_SCORE[group_score], 1 if renormalize else 0, _ptr(topk_ids),
+        _ptr(topk_w), _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(workspace), ws_bytes,
+        _stream(stream)))
     return topk_ids, topk_w, expert_offsets, sorted_pairs
 
 

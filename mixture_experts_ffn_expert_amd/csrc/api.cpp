@@ -181,6 +181,58 @@ moe_status moe_route(const float* logits, int T, int E, int K, int32_t* topk_ids
                                           sorted_pairs, ws, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_route_scored(const float* logits, int T, int E, int K, moe_score score,
+                            const float* selection_bias, int n_group, int topk_group,
+                            moe_group_score group_score, int renormalize, int32_t* topk_ids,
+                            float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                            void* ws, size_t ws_bytes, moe_stream_t stream) {
+  const char* fn = "moe_route_scored";
+  clear_err();
+  if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
+  if (E < 1 || E > kMaxE) return fail(MOE_E_SHAPE, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if (K < 1 || K > E || K > kMaxK)
+    return fail(MOE_E_SHAPE, "%s: K=%d outside [1, min(E=%d, %d)]", fn, K, E, kMaxK);
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)
+    return fail(MOE_E_INVALID, "%s: score=%d is not MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID", fn,
+                (int)score);
+  if (group_score != MOE_GROUP_MAX && group_score != MOE_GROUP_TOP2_SUM)
+    return fail(MOE_E_INVALID, "%s: group_score=%d is not MOE_GROUP_MAX or MOE_GROUP_TOP2_SUM",
+                fn, (int)group_score);
+  if (renormalize != 0 && renormalize != 1)
+    return fail(MOE_E_INVALID, "%s: renormalize=%d must be 0 or 1", fn, renormalize);
+  if (n_group < 1 || n_group > 64 || E % n_group != 0)
+    return fail(MOE_E_SHAPE, "%s: n_group=%d must divide E=%d and lie in [1, 64]", fn, n_group,
+                E);
+  if (topk_group < 1 || topk_group > n_group)
+    return fail(MOE_E_SHAPE, "%s: topk_group=%d outside [1, n_group=%d]", fn, topk_group,
+                n_group);
+  if ((long long)topk_group * (E / n_group) < K)
+    return fail(MOE_E_SHAPE, "%s: %d groups of %d experts hold fewer than K=%d experts", fn,
+                topk_group, E / n_group, K);
+  if (!fits_i32((long long)T * E) || !fits_i32((long long)T * K))
+    return fail(MOE_E_SHAPE, "%s: T*E or T*K exceeds 2^31", fn);
+  if (ws_bytes < moe_route_workspace_bytes(T, E, K))
+    return fail(MOE_E_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, ws_bytes,
+                moe_route_workspace_bytes(T, E, K));
+  REQUIRE_NONNULL(fn, expert_offsets);
+  if (T == 0) return MOE_OK;  // nothing routed; no output is written
+  if (moe_route_workspace_bytes(T, E, K) > 0 && (ws == nullptr || (uintptr_t)ws % 4 != 0))
+    return fail(MOE_E_WORKSPACE, "%s: ws is NULL or not 4-byte aligned (%zu bytes needed)", fn,
+                moe_route_workspace_bytes(T, E, K));
+  REQUIRE_NONNULL(fn, logits);
+  REQUIRE_NONNULL(fn, topk_ids);
+  REQUIRE_NONNULL(fn, topk_w);
+  REQUIRE_NONNULL(fn, sorted_pairs);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(
+      fn, moe::launch_route_scored(logits, T, E, K, score == MOE_SCORE_SIGMOID ? 1 : 0,
+                                   selection_bias, n_group, topk_group,
+                                   group_score == MOE_GROUP_TOP2_SUM ? 1 : 0, renormalize,
+                                   topk_ids, topk_w, expert_offsets, sorted_pairs, ws,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w_gu,
                                         int E, int I, const int32_t* sorted_pairs,
                                         const int32_t* expert_offsets, int K, uint16_t* act,

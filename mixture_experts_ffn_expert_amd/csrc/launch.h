@@ -11,6 +11,10 @@ namespace moe {
 size_t route_workspace_bytes(int T, int E, int K);
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                         int32_t* offsets, int32_t* sorted, void* ws, hipStream_t s);
+hipError_t launch_route_scored(const float* logits, int T, int E, int K, int sigmoid,
+                               const float* bias, int n_group, int topk_group, int group_top2,
+                               int renorm, int32_t* ids, float* w, int32_t* offsets,
+                               int32_t* sorted, void* ws, hipStream_t s);
 
 // gemm.hip
 hipError_t launch_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w_gu, int E, int I,

@@ -123,6 +123,186 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   topk_token(logits + (size_t)t * E, E, K, ids + (size_t)t * K, w + (size_t)t * K);
 }
 
+// ---------------------------------------------------------------------------
+// General router: sigmoid or full-softmax scores, an optional selection bias
+// and group-limited selection (the grouped / biased / sigmoid forms that
+// issue #3094's row statement and PR #509's Honest gaps list as the router
+// gaps left; their arithmetic follows the DeepSeek-V2 / V3 technical
+// reports). Per token, in f32, each operation rounded on its own:
+//   s_e = sigmoid(l_e), or z_e / S with m = max l, z_e = exp(l_e - m) and S
+//       the butterfly sum (lane e%64 adds its z in increasing e, then lanes
+//       l and l^m are added for m = 32 .. 1);
+//   c_e = s_e (+ bias_e); NaN ranks as -inf;
+//   groups of E/n_group consecutive experts scored by their largest c or the
+//   sum of their two largest; the topk_group best groups stay allowed (ties
+//   to the lower group);
+//   K rounds pick the largest allowed c (ties to the lower id);
+//   w_k = s_{e_k}, renormalised by the sequential sum over k when asked.
+// ---------------------------------------------------------------------------
+struct ScoredRouter {
+  int sigmoid;          // 1: sigmoid scores, 0: softmax over all E
+  const float* bias;    // [E] selection bias or null
+  int n_group;          // 1: no group limit
+  int topk_group;       // groups kept
+  int group_top2;       // 1: group score = sum of its two largest c, 0: largest c
+  int renorm;           // 1: renormalise the K weights
+};
+
+__device__ __forceinline__ uint32_t select_key(float c) {
+  if (c != c) c = -__builtin_inff();  // NaN ranks as -inf
+  if (c == 0.0f) c = 0.0f;            // -0 ties with +0
+  return order_key(c);
+}
+
+__device__ __forceinline__ void topk_scored_token(const float* __restrict__ row, int E, int K,
+                                                  const ScoredRouter& r,
+                                                  int32_t* __restrict__ ids,
+                                                  float* __restrict__ w) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int nper = (E + 63) >> 6;
+  float s[kMaxPerLane];
+  uint32_t key[kMaxPerLane];
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    const int e = lane + 64 * j;
+    float x = -__builtin_inff();
+    if (j < nper && e < E) {
+      x = row[e];
+      if (x != x) x = -__builtin_inff();
+    }
+    s[j] = x;  // logits for now
+  }
+  if (r.sigmoid) {
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) s[j] = sigmoid_cw(s[j]);
+  } else {
+    uint32_t mk = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j)
+      if (j < nper && lane + 64 * j < E) mk = max(mk, select_key(s[j]));
+    const float m = key_value(__ockl_wfred_max_u32(mk));
+    float p = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      if (j < nper && lane + 64 * j < E) {
+        const float z = exp_cw(s[j] - m);
+        s[j] = z;
+        p = (j == 0) ? z : p + z;
+      }
+    }
+#pragma unroll
+    for (int m2 = 32; m2 >= 1; m2 >>= 1) p = p + __shfl_xor(p, m2);
+    const float S = lane_f32(p, 0);
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j)
+      if (j < nper && lane + 64 * j < E) s[j] = __fdiv_rn(s[j], S);
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) {
+    const int e = lane + 64 * j;
+    uint32_t kj = 0;
+    if (j < nper && e < E) kj = select_key(r.bias != nullptr ? s[j] + r.bias[e] : s[j]);
+    key[j] = kj;
+  }
+
+  if (r.n_group > 1) {
+    const int gs = E / r.n_group;
+    uint32_t gkey = 0;  // lane g holds group g's score key
+    for (int g = 0; g < r.n_group; ++g) {
+      const int lo = g * gs, hi = lo + gs;
+      uint32_t mk = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxPerLane; ++j) {
+        const int e = lane + 64 * j;
+        if (e >= lo && e < hi) mk = max(mk, key[j]);
+      }
+      const uint32_t M1 = __ockl_wfred_max_u32(mk);
+      float score = key_value(M1);
+      if (r.group_top2 && gs > 1) {
+        // drop one instance of the largest (the lowest id holding it)
+        int first = -1;
+#pragma unroll
+        for (int j = 0; j < kMaxPerLane; ++j) {
+          const int e = lane + 64 * j;
+          const uint64_t hit = __ballot(e >= lo && e < hi && key[j] == M1);
+          if (first < 0 && hit) first = (__ffsll((long long)hit) - 1) + 64 * j;
+        }
+        uint32_t mk2 = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxPerLane; ++j) {
+          const int e = lane + 64 * j;
+          if (e >= lo && e < hi && e != first) mk2 = max(mk2, key[j]);
+        }
+        score = score + key_value(__ockl_wfred_max_u32(mk2));
+      }
+      if (lane == g) gkey = select_key(score);
+    }
+    uint64_t keep = 0;
+    for (int k = 0; k < r.topk_group; ++k) {
+      const uint32_t M = __ockl_wfred_max_u32(gkey);
+      const uint64_t hit = __ballot(gkey == M && gkey != 0);
+      const int g = __ffsll((long long)hit) - 1;
+      keep |= 1ull << g;
+      if (lane == g) gkey = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && !((keep >> (e / gs)) & 1ull)) key[j] = 0;
+    }
+  }
+
+  float my_s = 0.0f;  // lane k keeps the k-th selected score
+  int my_id = 0;
+  for (int k = 0; k < K; ++k) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) m = max(m, key[j]);
+    const uint32_t M = __ockl_wfred_max_u32(m);
+    int sel = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      if (j >= nper) break;
+      const uint64_t hit = __ballot(key[j] == M);
+      if (hit) {
+        sel = (__ffsll((long long)hit) - 1) + 64 * j;
+        break;
+      }
+    }
+    float sv = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      if (sel == lane + 64 * j) key[j] = 0;  // taken
+      if (j == (sel >> 6)) sv = s[j];
+    }
+    const float s_sel = lane_f32(sv, sel & 63);
+    if (lane == k) {
+      my_s = s_sel;
+      my_id = sel;
+    }
+  }
+  float wk = my_s;
+  if (r.renorm) {
+    float S = lane_f32(my_s, 0);
+    for (int k = 1; k < K; ++k) S = S + lane_f32(my_s, k);
+    wk = __fdiv_rn(my_s, S);
+  }
+  if (lane < K) {
+    ids[lane] = my_id;
+    w[lane] = wk;
+  }
+}
+
+__global__ __launch_bounds__(256) void topk_scored_kernel(const float* __restrict__ logits, int T,
+                                                          int E, int K, ScoredRouter r,
+                                                          int32_t* __restrict__ ids,
+                                                          float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave leaves together
+  topk_scored_token(logits + (size_t)t * E, E, K, r, ids + (size_t)t * K, w + (size_t)t * K);
+}
+
 constexpr int kGroupWaves = 8;
 // Pairs per workgroup segment of the multi-workgroup grouping (and the
 // largest pair count the single-workgroup kernel handles).
@@ -305,10 +485,9 @@ size_t route_workspace_bytes(int T, int E, int K) {
   return (size_t)(nseg * E * 4);
 }
 
-hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w,
-                        int32_t* offsets, int32_t* sorted, void* ws, hipStream_t s) {
-  const int P = T * K;
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
+// Stable grouping of the P = T*K routed pairs by expert.
+static hipError_t launch_grouping(const int32_t* ids, int P, int E, int32_t* offsets,
+                                  int32_t* sorted, void* ws, hipStream_t s) {
   if (P <= kGroupSeg) {
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupWaves * 64), 0, s, ids, P, E, offsets,
                        sorted);
@@ -322,6 +501,26 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, 
                        cnt, sorted);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w,
+                        int32_t* offsets, int32_t* sorted, void* ws, hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_grouping(ids, T * K, E, offsets, sorted, ws, s);
+}
+
+hipError_t launch_route_scored(const float* logits, int T, int E, int K, int sigmoid,
+                               const float* bias, int n_group, int topk_group, int group_top2,
+                               int renorm, int32_t* ids, float* w, int32_t* offsets,
+                               int32_t* sorted, void* ws, hipStream_t s) {
+  const ScoredRouter r{sigmoid, bias, n_group, topk_group, group_top2, renorm};
+  hipLaunchKernelGGL(topk_scored_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, r,
+                     ids, w);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_grouping(ids, T * K, E, offsets, sorted, ws, s);
 }
 
 }  // namespace moe

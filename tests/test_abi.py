@@ -175,3 +175,19 @@ def test_refused_gemm_call_disarms_timing(lib):
     assert lib.moe_time_next_gemm(A, A2) == 0
     assert lib.moe_grouped_gemm_down(A, 8, 16, A, 8, 20, A, A, None, A, None) == 3
     assert lib.moe_router_logits(None, 0, 16, None, 8, None, None, None) == 0
+
+
+@pytest.mark.parametrize("E,K,score,n_group,topk_group,gscore,renorm,status,word", [
+    (8, 2, 2, 1, 1, 0, 1, 1, "score"),
+    (8, 2, 0, 1, 1, 2, 1, 1, "group_score"),
+    (8, 2, 0, 1, 1, 0, 2, 1, "renormalize"),
+    (8, 2, 0, 3, 1, 0, 1, 3, "n_group"),          # 3 does not divide 8
+    (128, 2, 0, 128, 1, 0, 1, 3, "n_group"),      # more than 64 groups
+    (8, 2, 0, 4, 5, 0, 1, 3, "topk_group"),
+    (8, 5, 1, 4, 2, 1, 1, 3, "fewer than K"),     # 2 groups of 2 hold 4 experts
+])
+def test_route_scored_refusals(lib, E, K, score, n_group, topk_group, gscore, renorm, status,
+                               word):
+    st = lib.moe_route_scored(A, 4, E, K, score, None, n_group, topk_group, gscore, renorm,
+                              A, A, A, A, None, 0, None)
+    assert st == status and word in _err(lib) and "moe_route_scored" in _err(lib)
