@@ -17,10 +17,12 @@ distinct weights. `hipgraph` times the same steps captured once into a HIP
 graph and replayed.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
-       (--workload picks one of the five workloads, default 2: the 32-token
-       decode layer with 128 experts, top-8).
+       (--workload picks one of the six workloads, default 2: the 32-token
+       decode layer with 128 experts, top-8; 6 is the 256-expert layer with
+       the grouped sigmoid router).
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -99,8 +101,7 @@ def cpu_baseline(d, sample_tokens):
     sub = dict(d)
     sub["x"] = d["x"][:sample_tokens]
     cfg = d["cfg"]
-    sub["cfg"] = workloads.MoeConfig(cfg.name, sample_tokens, cfg.H, cfg.E, cfg.K, cfg.I,
-                                     cfg.I_s, cfg.skew_bias)
+    sub["cfg"] = dataclasses.replace(cfg, T=sample_tokens)
     t0 = time.perf_counter()
     oracle.moe_layer(sub)
     dt = time.perf_counter() - t0
@@ -160,6 +161,13 @@ def main():
 
     x = bf(d["x"])
     bias = torch.from_numpy(d["router_bias"]).to(dev) if "router_bias" in d else None
+    router = workloads.router_args(cfg)
+    routed_scale = 1.0
+    sel_bias = None
+    if router is not None:
+        router = dict(router)
+        routed_scale = router.pop("routed_scale")
+        sel_bias = torch.from_numpy(d["selection_bias"]).to(dev)
     # one weight set per layer: the same values at distinct addresses, as
     # consecutive MoE layers of a model hold distinct weights
     names = [n for n in ("w_r", "w_gu", "w_d", "w_gu_s", "w_d_s", "w_g") if n in d]
@@ -185,8 +193,14 @@ def main():
         w_gu_s, w_d_s, w_g = lw.get("w_gu_s"), lw.get("w_d_s"), lw.get("w_g")
         logits = moe.moe_router_logits(x, w_r, bias, bufs.get("logits"))
         bufs["logits"] = logits
-        ids, w, off, sp = moe.moe_route(logits, K, bufs.get("ids"), bufs.get("w"),
-                                        bufs.get("offsets"), bufs.get("sorted"), ws)
+        if router is None:
+            ids, w, off, sp = moe.moe_route(logits, K, bufs.get("ids"), bufs.get("w"),
+                                            bufs.get("offsets"), bufs.get("sorted"), ws)
+        else:
+            ids, w, off, sp = moe.moe_route_scored(
+                logits, K, selection_bias=sel_bias, **router, topk_ids=bufs.get("ids"),
+                topk_w=bufs.get("w"), expert_offsets=bufs.get("offsets"),
+                sorted_pairs=bufs.get("sorted"), workspace=ws)
         bufs.update(ids=ids, w=w, offsets=off, sorted=sp)
         if record:
             # the GEMM kernels record their own start and end (no packets
@@ -209,7 +223,7 @@ def main():
                                            bufs.get("sd"))
             gl = moe.moe_router_logits(x, w_g.view(1, H), None, bufs.get("gl"))
             bufs.update(sd_act=sa, sd=sd, gl=gl)
-        out = moe.moe_combine_gate(eo, T, K, None, 1.0, sd, gl, bufs.get("out"))
+        out = moe.moe_combine_gate(eo, T, K, None, routed_scale, sd, gl, bufs.get("out"))
         bufs["out"] = out
 
     L = len(layers)
@@ -279,7 +293,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1/fan_in) bf16 weights of the workload's shapes)",
         "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "K": K, "I": I,
-                   "I_shared": cfg.I_s, "skewed_router": cfg.skew_bias,
+                   "I_shared": cfg.I_s, "skewed_router": cfg.skew_bias, "router": cfg.router,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "grouped_gemm": {
@@ -296,7 +310,7 @@ def main():
     if not args.no_cpu_baseline:
         # about 10-30 s of CPU work at most: all tokens of the small workloads,
         # a prefix of the large ones
-        sample = {1: 16, 2: 32, 3: 256, 4: 128, 5: 64}.get(args.workload, 32)
+        sample = {1: 16, 2: 32, 3: 256, 4: 128, 5: 64, 6: 128}.get(args.workload, 32)
         res["cpu_baseline"] = cpu_baseline(d, min(sample, T))
     print(json.dumps(res))
 

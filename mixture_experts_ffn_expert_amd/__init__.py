@@ -322,9 +322,12 @@ def moe_combine_gate(expert_out, T, K, topk_w=None, routed_scale=1.0, shared=Non
 
 
 def moe_layer(x, w_r, w_gu, w_d, K, router_bias=None, w_gu_s=None, w_d_s=None, w_g=None,
-              bufs=None, stream=None):
+              bufs=None, stream=None, router=None, selection_bias=None, routed_scale=1.0):
     """Enqueue one MoE layer: logits, route, gate-up, down, (shared), combine.
 
+    ``router`` (dict of ``moe_route_scored`` keyword arguments: score,
+    n_group, topk_group, group_score, renormalize) selects the general router
+    with ``selection_bias``; None routes with the ungrouped softmax top-k.
     ``bufs`` (dict) may hold preallocated outputs/intermediates under the keys
     logits, ids, w, offsets, sorted, act, expert_out, sd_act, sd, gl, out; the
     dict is filled with everything produced. Returns the bf16 [T, H] output.
@@ -344,10 +347,15 @@ def moe_layer(x, w_r, w_gu, w_d, K, router_bias=None, w_gu_s=None, w_d_s=None, w
     logits = moe_router_logits(x, w_r, router_bias, buf("logits", (T, E), torch.float32), stream)
     ws_bytes = moe_route_workspace_bytes(T, E, K)
     ws = buf("route_ws", (ws_bytes,), torch.uint8) if ws_bytes else None
-    ids, w, off, sp = moe_route(logits, K, buf("ids", (T, K), torch.int32),
-                                buf("w", (T, K), torch.float32),
-                                buf("offsets", (E + 1,), torch.int32),
-                                buf("sorted", (T * K,), torch.int32), ws, stream=stream)
+    outs = (buf("ids", (T, K), torch.int32), buf("w", (T, K), torch.float32),
+            buf("offsets", (E + 1,), torch.int32), buf("sorted", (T * K,), torch.int32))
+    if router is None:
+        ids, w, off, sp = moe_route(logits, K, *outs, ws, stream=stream)
+    else:
+        ids, w, off, sp = moe_route_scored(logits, K, selection_bias=selection_bias, **router,
+                                           topk_ids=outs[0], topk_w=outs[1],
+                                           expert_offsets=outs[2], sorted_pairs=outs[3],
+                                           workspace=ws, stream=stream)
     act = moe_grouped_gemm_gateup_silu(x, w_gu, sp, off, K, buf("act", (T * K, I), torch.bfloat16),
                                        stream)
     eo = moe_grouped_gemm_down(act, w_d, sp, off, w, buf("expert_out", (T * K, H), torch.bfloat16),
@@ -360,5 +368,5 @@ def moe_layer(x, w_r, w_gu, w_d, K, router_bias=None, w_gu_s=None, w_d_s=None, w
         sd = moe_grouped_gemm_down(sa, w_d_s.view(1, H, Is), None, None, None,
                                    buf("sd", (T, H), torch.bfloat16), stream)
         gl = moe_router_logits(x, w_g.view(1, H), None, buf("gl", (T, 1), torch.float32), stream)
-    return moe_combine_gate(eo, T, K, None, 1.0, sd, gl, buf("out", (T, H), torch.bfloat16),
-                            stream=stream)
+    return moe_combine_gate(eo, T, K, None, routed_scale, sd, gl,
+                            buf("out", (T, H), torch.bfloat16), stream=stream)

@@ -155,7 +155,7 @@ __device__ __forceinline__ uint32_t select_key(float c) {
 }
 
 __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row, int E, int K,
-                                                  const ScoredRouter& r,
+                                                  const ScoredRouter& r, uint32_t* gkeys,
                                                   int32_t* __restrict__ ids,
                                                   float* __restrict__ w) {
 #pragma clang fp contract(off)
@@ -175,17 +175,23 @@ __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row,
   }
   if (r.sigmoid) {
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) s[j] = sigmoid_cw(s[j]);
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      if (j >= nper) break;
+      s[j] = sigmoid_cw(s[j]);
+    }
   } else {
     uint32_t mk = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j)
-      if (j < nper && lane + 64 * j < E) mk = max(mk, select_key(s[j]));
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      if (j >= nper) break;
+      if (lane + 64 * j < E) mk = max(mk, select_key(s[j]));
+    }
     const float m = key_value(__ockl_wfred_max_u32(mk));
     float p = 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
-      if (j < nper && lane + 64 * j < E) {
+      if (j >= nper) break;
+      if (lane + 64 * j < E) {
         const float z = exp_cw(s[j] - m);
         s[j] = z;
         p = (j == 0) ? z : p + z;
@@ -195,48 +201,47 @@ __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row,
     for (int m2 = 32; m2 >= 1; m2 >>= 1) p = p + __shfl_xor(p, m2);
     const float S = lane_f32(p, 0);
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j)
-      if (j < nper && lane + 64 * j < E) s[j] = __fdiv_rn(s[j], S);
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      if (j >= nper) break;
+      if (lane + 64 * j < E) s[j] = __fdiv_rn(s[j], S);
+    }
   }
 #pragma unroll
+  for (int j = 0; j < kMaxPerLane; ++j) key[j] = 0;
+#pragma unroll
   for (int j = 0; j < kMaxPerLane; ++j) {
+    if (j >= nper) break;
     const int e = lane + 64 * j;
-    uint32_t kj = 0;
-    if (j < nper && e < E) kj = select_key(r.bias != nullptr ? s[j] + r.bias[e] : s[j]);
-    key[j] = kj;
+    if (e < E) key[j] = select_key(r.bias != nullptr ? s[j] + r.bias[e] : s[j]);
   }
 
   if (r.n_group > 1) {
+    // Group scores: the selection keys go through LDS, and lane g < n_group
+    // scans its group's E/n_group keys for the largest two.
     const int gs = E / r.n_group;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+      if (j >= nper) break;
+      if (lane + 64 * j < E) gkeys[lane + 64 * j] = key[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     uint32_t gkey = 0;  // lane g holds group g's score key
-    for (int g = 0; g < r.n_group; ++g) {
-      const int lo = g * gs, hi = lo + gs;
-      uint32_t mk = 0;
-#pragma unroll
-      for (int j = 0; j < kMaxPerLane; ++j) {
-        const int e = lane + 64 * j;
-        if (e >= lo && e < hi) mk = max(mk, key[j]);
-      }
-      const uint32_t M1 = __ockl_wfred_max_u32(mk);
-      float score = key_value(M1);
-      if (r.group_top2 && gs > 1) {
-        // drop one instance of the largest (the lowest id holding it)
-        int first = -1;
-#pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j) {
-          const int e = lane + 64 * j;
-          const uint64_t hit = __ballot(e >= lo && e < hi && key[j] == M1);
-          if (first < 0 && hit) first = (__ffsll((long long)hit) - 1) + 64 * j;
+    if (lane < r.n_group) {
+      uint32_t k1 = 0, k2 = 0;  // largest and second largest key of the group
+      for (int i = 0; i < gs; ++i) {
+        const uint32_t v = gkeys[lane * gs + i];
+        if (v > k1) {
+          k2 = k1;
+          k1 = v;
+        } else if (v > k2) {
+          k2 = v;
         }
-        uint32_t mk2 = 0;
-#pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j) {
-          const int e = lane + 64 * j;
-          if (e >= lo && e < hi && e != first) mk2 = max(mk2, key[j]);
-        }
-        score = score + key_value(__ockl_wfred_max_u32(mk2));
       }
-      if (lane == g) gkey = select_key(score);
+      float score = key_value(k1);
+      if (r.group_top2 && gs > 1) score = score + key_value(k2);
+      gkey = select_key(score);
     }
     uint64_t keep = 0;
     for (int k = 0; k < r.topk_group; ++k) {
@@ -298,9 +303,11 @@ __global__ __launch_bounds__(256) void topk_scored_kernel(const float* __restric
                                                           int E, int K, ScoredRouter r,
                                                           int32_t* __restrict__ ids,
                                                           float* __restrict__ w) {
+  __shared__ uint32_t gkeys[4][kMaxE];  // per wave: selection keys for the group scores
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together
-  topk_scored_token(logits + (size_t)t * E, E, K, r, ids + (size_t)t * K, w + (size_t)t * K);
+  topk_scored_token(logits + (size_t)t * E, E, K, r, gkeys[threadIdx.x >> 6], ids + (size_t)t * K,
+                    w + (size_t)t * K);
 }
 
 constexpr int kGroupWaves = 8;

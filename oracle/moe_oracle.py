@@ -486,22 +486,31 @@ def moe_layer(inp: dict, logits=None, keep: bool = False) -> dict:
 
     logits defaults to ``router_logits(x, W_r, bias)``; pass the f32 logits to
     route on a given array. The routed outputs carry their weight from the
-    down-projection, so the combine runs unweighted (N3) with routed_scale 1,
-    plus the sigmoid-gated shared expert when the workload has one.
+    down-projection, so the combine runs unweighted (N3) with routed_scale 1
+    (2.5 with the grouped sigmoid router), plus the sigmoid-gated shared
+    expert when the workload has one.
     """
     cfg = inp["cfg"]
     T, K, H, E = cfg.T, cfg.K, cfg.H, cfg.E
     x = inp["x"]
     if logits is None:
         logits = router_logits(x, inp["w_r"], inp.get("router_bias"))
-    ids, w, offsets, sorted_pairs = route(logits, K)
+    routed_scale = 1.0
+    if getattr(cfg, "router", "softmax") == "grouped_sigmoid":
+        # sigmoid scores, selection bias, 8 groups keep 4 by top-2 sums,
+        # renormalised, routed scale 2.5 (see route_scored)
+        ids, w, offsets, sorted_pairs = route_scored(logits, K, "sigmoid",
+                                                     inp["selection_bias"], 8, 4, "top2", True)
+        routed_scale = 2.5
+    else:
+        ids, w, offsets, sorted_pairs = route(logits, K)
     act = gateup_silu(x, inp["w_gu"], sorted_pairs, offsets, K)
     eo = down_proj(act, inp["w_d"], sorted_pairs, offsets, w)
     sd = gl = None
     if "w_gu_s" in inp:
         sd = shared_expert(x, inp["w_gu_s"], inp["w_d_s"])
         gl = gate_logit(x, inp["w_g"])
-    out = combine_gate(eo, T, K, H, None, 1.0, sd, gl)
+    out = combine_gate(eo, T, K, H, None, routed_scale, sd, gl)
     res = {"logits": logits, "ids": ids, "w": w, "offsets": offsets,
            "sorted_pairs": sorted_pairs, "out": out}
     if keep:

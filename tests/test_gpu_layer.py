@@ -19,6 +19,7 @@ import pytest
 import torch
 
 import oracle as O
+import workloads as W
 from conftest import cached_inputs
 from gpu_helpers import (DEV, assert_bits_equal, assert_gemm_close, bits, sample_rows, sub_down,
                          sub_gateup, to_dev_bf16)
@@ -33,14 +34,21 @@ def _dev_inputs(d):
     t["router_bias"] = None
     if "router_bias" in d:
         t["router_bias"] = torch.from_numpy(d["router_bias"]).to(DEV)
+    t["selection_bias"] = None
+    if "selection_bias" in d:
+        t["selection_bias"] = torch.from_numpy(d["selection_bias"]).to(DEV)
+    t["router"] = W.router_args(d["cfg"])
     for k in ("w_gu_s", "w_d_s", "w_g"):
         t[k] = to_dev_bf16(d[k]) if k in d else None
     return t
 
 
 def _run(t, K, bufs=None):
+    router = None if t["router"] is None else dict(t["router"])
+    scale = 1.0 if router is None else router.pop("routed_scale")
     return moe.moe_layer(t["x"], t["w_r"], t["w_gu"], t["w_d"], K, t["router_bias"], t["w_gu_s"],
-                         t["w_d_s"], t["w_g"], bufs=bufs)
+                         t["w_d_s"], t["w_g"], bufs=bufs, router=router,
+                         selection_bias=t["selection_bias"], routed_scale=scale)
 
 
 def _routing_flips_are_near_ties(gpu_logits, ref_logits, K):
@@ -56,7 +64,7 @@ def _routing_flips_are_near_ties(gpu_logits, ref_logits, K):
     return int(diff.sum())
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 6])
 def test_layer_end_to_end(gpu_lib, n):
     d = cached_inputs(n)
     cfg = d["cfg"]
@@ -85,16 +93,18 @@ def test_layer_end_to_end(gpu_lib, n):
         assert_gemm_close(sd, O.down_proj(sa, d["w_d_s"][None], None, None, None), "shared out")
         gl = bits(bufs["gl"]).reshape(-1)
         assert np.max(np.abs(gl.astype(np.float64) - ref["gl"])) <= 1e-4 * np.max(np.abs(ref["gl"])) + 1e-6
-    assert_bits_equal(bits(out), O.combine_gate(eo, cfg.T, cfg.K, cfg.H, None, 1.0, sd, gl),
+    scale = 1.0 if t["router"] is None else t["router"]["routed_scale"]
+    assert_bits_equal(bits(out), O.combine_gate(eo, cfg.T, cfg.K, cfg.H, None, scale, sd, gl),
                       "combine")
     g = O.f32_from_bf16(bits(out)).astype(np.float64)
     r = O.f32_from_bf16(ref["out"]).astype(np.float64)
     nmse = float(np.sum((g - r) ** 2) / np.sum(r * r))
     assert nmse <= 1e-5, f"layer chain NMSE {nmse:.3e}"
     # the oracle's own logits route the same way except at near-ties
-    o_logits = O.router_logits(d["x"], d["w_r"], d.get("router_bias"))
-    flips = _routing_flips_are_near_ties(g_logits, o_logits, cfg.K)
-    print(f"cfg{n}: tokens routed differently on own logits: {flips}")
+    if t["router"] is None:
+        o_logits = O.router_logits(d["x"], d["w_r"], d.get("router_bias"))
+        flips = _routing_flips_are_near_ties(g_logits, o_logits, cfg.K)
+        print(f"cfg{n}: tokens routed differently on own logits: {flips}")
 
 
 def test_layer_skewed_full_size_sampled(gpu_lib):

@@ -95,6 +95,27 @@ def test_dense_brute_force_skewed_small_layer():
     assert len(set(np.diff(res["offsets"]).tolist())) > 1
 
 
+def test_dense_brute_force_grouped_sigmoid_small_layer():
+    """The grouped sigmoid router in a small layer: selection within the 4 kept
+    groups of 2, unbiased renormalised weights, routed scale 2.5."""
+    cfg = W.MoeConfig("small_grouped", 24, 32, 16, 4, 16, I_s=16, router="grouped_sigmoid")
+    d = W.make_inputs(cfg, seed=22)
+    res = O.moe_layer(d, keep=True)
+    s = O.router_scores(res["logits"], "sigmoid").astype(np.float64)
+    c = s + d["selection_bias"].astype(np.float64)
+    for t in range(cfg.T):
+        groups = sorted(range(8), key=lambda g: (-(np.sort(c[t, 2 * g:2 * g + 2])[::-1].sum()), g))
+        allowed = [e for e in range(16) if e // 2 in groups[:4]]
+        want = sorted(allowed, key=lambda e: (-c[t, e], e))[:4]
+        assert res["ids"][t].tolist() == want
+        ws = s[t, res["ids"][t]]
+        assert np.allclose(res["w"][t], ws / ws.sum(), rtol=1e-6, atol=0)
+    eo, sd, gl = _dense_brute_force(d, res["ids"], res["w"])
+    assert np.array_equal(res["expert_out"].reshape(cfg.T, cfg.K, cfg.H), eo)
+    out = O.combine_gate(eo, cfg.T, cfg.K, cfg.H, None, 2.5, sd, gl)
+    assert np.array_equal(res["out"], out)
+
+
 def _identical_experts(seed=3):
     cfg = W.MoeConfig("identical", 20, 64, 8, 3, 32)
     d = W.make_inputs(cfg, seed=seed)

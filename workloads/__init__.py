@@ -16,6 +16,7 @@ Recipe (one numpy ``SeedSequence(seed)``, children spawned in a fixed order):
   child 5  W_d_s  [H,I_s]      ~ N(0,1/I_s)
   child 6  w_g    [H]          ~ N(0,1/H)   (shared-expert gate vector)
   child 7  ranking             permutation of E experts (skewed router only)
+  child 8  selection bias [E] ~ N(0, 0.1^2) float32 (grouped sigmoid router only)
 
 N(0, v) names the variance, so the standard deviation is 1/sqrt(fan_in). Each
 value is drawn as float32 by PCG64, multiplied by float32(1/sqrt(fan_in)) and
@@ -25,6 +26,7 @@ computed in float64 and stored as float32.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -43,6 +45,11 @@ class MoeConfig:
     I: int
     I_s: int = 0          # shared-expert intermediate size (0: no shared expert)
     skew_bias: bool = False  # router bias 2*ln(1/rank_e)
+    # "softmax": ungrouped softmax top-k, renormalised. "grouped_sigmoid":
+    # sigmoid scores, a per-expert selection bias, 8 groups of which the 4
+    # with the largest top-2 sums stay allowed, renormalised weights and a
+    # routed scale of 2.5 in the combine (the DeepSeek-V3 router shape).
+    router: str = "softmax"
 
     @property
     def P(self) -> int:
@@ -52,13 +59,26 @@ class MoeConfig:
 # The five workloads: a tiny layer with a shared expert, a 128-expert top-8
 # decode layer and the same layer in prefill, a 256-expert layer with a gated
 # shared expert, and a large layer whose router bias makes routing Zipf-skewed.
+# A sixth has the 256-expert layer's shapes with the grouped sigmoid router.
 CONFIGS = {
     1: MoeConfig("tiny_T16_H64_E8_K2_I32_shared32", 16, 64, 8, 2, 32, I_s=32),
     2: MoeConfig("decode_T32_H2048_E128_K8_I768", 32, 2048, 128, 8, 768),
     3: MoeConfig("prefill_T4096_H2048_E128_K8_I768", 4096, 2048, 128, 8, 768),
     4: MoeConfig("shared_T512_H2048_E256_K8_I512_shared512", 512, 2048, 256, 8, 512, I_s=512),
     5: MoeConfig("skewed_T8192_H4096_E128_K8_I1536", 8192, 4096, 128, 8, 1536, skew_bias=True),
+    6: MoeConfig("grouped_T512_H2048_E256_K8_I512_shared512", 512, 2048, 256, 8, 512, I_s=512,
+                 router="grouped_sigmoid"),
 }
+
+
+def router_args(cfg) -> dict:
+    """Router form of a workload, as keyword arguments of the general router
+    (score, n_group, topk_group, group_score, renormalize) plus the combine's
+    routed_scale; None for the ungrouped softmax router."""
+    if config(cfg).router == "softmax":
+        return None
+    return {"score": "sigmoid", "n_group": 8, "topk_group": 4, "group_score": "top2",
+            "renormalize": True, "routed_scale": 2.5}
 
 
 def config(n_or_cfg) -> MoeConfig:
@@ -115,10 +135,10 @@ def make_inputs(cfg, seed: int | None = None, *, T: int | None = None,
     if seed is None:
         seed = next((k for k, v in CONFIGS.items() if v == cfg), 0)
     if T is not None:
-        cfg = MoeConfig(cfg.name + f"_T{T}", T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.I_s, cfg.skew_bias)
+        cfg = dataclasses.replace(cfg, name=cfg.name + f"_T{T}", T=T)
     threads = _threads() if threads is None else threads
     H, E, I, I_s = cfg.H, cfg.E, cfg.I, cfg.I_s
-    kids = np.random.SeedSequence(seed).spawn(8)
+    kids = np.random.SeedSequence(seed).spawn(9)
     d = {"cfg": cfg, "seed": seed}
     d["x"] = _normal_bf16(kids[0], (cfg.T, H), 1.0)
     d["w_r"] = _normal_bf16(kids[1], (E, H), 1.0 / math.sqrt(H))
@@ -133,6 +153,9 @@ def make_inputs(cfg, seed: int | None = None, *, T: int | None = None,
         perm = np.random.Generator(np.random.PCG64(kids[7])).permutation(E)
         rank = 1.0 + perm.astype(np.float64)
         d["router_bias"] = (2.0 * np.log(1.0 / rank)).astype(np.float32)
+    if cfg.router == "grouped_sigmoid":
+        g = np.random.Generator(np.random.PCG64(kids[8]))
+        d["selection_bias"] = g.standard_normal(E, dtype=np.float32) * np.float32(0.1)
     return d
 
 
