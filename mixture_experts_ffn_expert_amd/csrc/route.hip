@@ -52,13 +52,14 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 // logit except that -0 reads as +0, which changes no weight (x - (+-0) and
 // (+-0) - (+-0) give the same exp argument up to the sign of zero, and
 // exp(+-0) = 1).
+template <int NP>
 __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int K,
                                            int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int nper = (E + 63) >> 6;
-  uint32_t key[kMaxPerLane];
+  uint32_t key[NP];
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
+  for (int j = 0; j < NP; ++j) {
     const int e = lane + 64 * j;
     uint32_t kj = 0;
     if (j < nper && e < E) {
@@ -74,12 +75,12 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
   for (int k = 0; k < K; ++k) {
     uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) m = max(m, key[j]);
+    for (int j = 0; j < NP; ++j) m = max(m, key[j]);
     const uint32_t M = __ockl_wfred_max_u32(m);
     // the lowest expert id holding the maximum: lower j first, then lower lane
     int sel = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (j >= nper) break;
       const uint64_t hit = __ballot(key[j] == M);
       if (hit) {
@@ -88,7 +89,7 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
       }
     }
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j)
+    for (int j = 0; j < NP; ++j)
       if (sel == lane + 64 * j) key[j] = 0;  // taken
     if (lane == k) {
       my_key = M;
@@ -115,12 +116,13 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ row, int E,
   }
 }
 
+template <int NP>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int K, int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together
-  topk_token(logits + (size_t)t * E, E, K, ids + (size_t)t * K, w + (size_t)t * K);
+  topk_token<NP>(logits + (size_t)t * E, E, K, ids + (size_t)t * K, w + (size_t)t * K);
 }
 
 // ---------------------------------------------------------------------------
@@ -154,6 +156,7 @@ __device__ __forceinline__ uint32_t select_key(float c) {
   return order_key(c);
 }
 
+template <int NP>
 __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row, int E, int K,
                                                   const ScoredRouter& r, uint32_t* gkeys,
                                                   int32_t* __restrict__ ids,
@@ -161,10 +164,10 @@ __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row,
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int nper = (E + 63) >> 6;
-  float s[kMaxPerLane];
-  uint32_t key[kMaxPerLane];
+  float s[NP];
+  uint32_t key[NP];
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
+  for (int j = 0; j < NP; ++j) {
     const int e = lane + 64 * j;
     float x = -__builtin_inff();
     if (j < nper && e < E) {
@@ -175,21 +178,21 @@ __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row,
   }
   if (r.sigmoid) {
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (j >= nper) break;
       s[j] = sigmoid_cw(s[j]);
     }
   } else {
     uint32_t mk = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (j >= nper) break;
       if (lane + 64 * j < E) mk = max(mk, select_key(s[j]));
     }
     const float m = key_value(__ockl_wfred_max_u32(mk));
     float p = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (j >= nper) break;
       if (lane + 64 * j < E) {
         const float z = exp_cw(s[j] - m);
@@ -201,15 +204,15 @@ __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row,
     for (int m2 = 32; m2 >= 1; m2 >>= 1) p = p + __shfl_xor(p, m2);
     const float S = lane_f32(p, 0);
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (j >= nper) break;
       if (lane + 64 * j < E) s[j] = __fdiv_rn(s[j], S);
     }
   }
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) key[j] = 0;
+  for (int j = 0; j < NP; ++j) key[j] = 0;
 #pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
+  for (int j = 0; j < NP; ++j) {
     if (j >= nper) break;
     const int e = lane + 64 * j;
     if (e < E) key[j] = select_key(r.bias != nullptr ? s[j] + r.bias[e] : s[j]);
@@ -220,7 +223,7 @@ __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row,
     // scans its group's E/n_group keys for the largest two.
     const int gs = E / r.n_group;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (j >= nper) break;
       if (lane + 64 * j < E) gkeys[lane + 64 * j] = key[j];
     }
@@ -252,7 +255,7 @@ __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row,
       if (lane == g) gkey = 0;
     }
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NP; ++j) {
       const int e = lane + 64 * j;
       if (e < E && !((keep >> (e / gs)) & 1ull)) key[j] = 0;
     }
@@ -263,11 +266,11 @@ __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row,
   for (int k = 0; k < K; ++k) {
     uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) m = max(m, key[j]);
+    for (int j = 0; j < NP; ++j) m = max(m, key[j]);
     const uint32_t M = __ockl_wfred_max_u32(m);
     int sel = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (j >= nper) break;
       const uint64_t hit = __ballot(key[j] == M);
       if (hit) {
@@ -277,7 +280,7 @@ __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row,
     }
     float sv = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
+    for (int j = 0; j < NP; ++j) {
       if (sel == lane + 64 * j) key[j] = 0;  // taken
       if (j == (sel >> 6)) sv = s[j];
     }
@@ -299,6 +302,7 @@ __device__ __forceinline__ void topk_scored_token(const float* __restrict__ row,
   }
 }
 
+template <int NP>
 __global__ __launch_bounds__(256) void topk_scored_kernel(const float* __restrict__ logits, int T,
                                                           int E, int K, ScoredRouter r,
                                                           int32_t* __restrict__ ids,
@@ -306,8 +310,8 @@ __global__ __launch_bounds__(256) void topk_scored_kernel(const float* __restric
   __shared__ uint32_t gkeys[4][kMaxE];  // per wave: selection keys for the group scores
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together
-  topk_scored_token(logits + (size_t)t * E, E, K, r, gkeys[threadIdx.x >> 6], ids + (size_t)t * K,
-                    w + (size_t)t * K);
+  topk_scored_token<NP>(logits + (size_t)t * E, E, K, r, gkeys[threadIdx.x >> 6],
+                        ids + (size_t)t * K, w + (size_t)t * K);
 }
 
 constexpr int kGroupWaves = 8;
@@ -369,13 +373,12 @@ __device__ __forceinline__ void count_segment(const int32_t* ids, int beg, int e
   __syncthreads();
 }
 
-// Single workgroup: counts, the exclusive scan over experts, then the scatter.
-__global__ __launch_bounds__(kGroupWaves * 64) void group_kernel(const int32_t* __restrict__ ids,
-                                                                 int P, int E,
-                                                                 int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ sorted) {
-  __shared__ int cur[kGroupWaves][kMaxE];  // per-wave counts, then per-wave cursors
-  __shared__ int wave_tot[kGroupWaves];
+// Single workgroup (kGroupWaves waves): counts, the exclusive scan over
+// experts, then the scatter. cur: per-wave counts, then per-wave cursors.
+__device__ __forceinline__ void group_block(const int32_t* __restrict__ ids, int P, int E,
+                                            int32_t* __restrict__ offsets,
+                                            int32_t* __restrict__ sorted, int (*cur)[kMaxE],
+                                            int* wave_tot) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -411,6 +414,15 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_kernel(const int32_t* 
   if (tid == 0) offsets[E] = P;
   __syncthreads();
   scatter_segment(ids, 0, P, E, cur, sorted);
+}
+
+__global__ __launch_bounds__(kGroupWaves * 64) void group_kernel(const int32_t* __restrict__ ids,
+                                                                 int P, int E,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ sorted) {
+  __shared__ int cur[kGroupWaves][kMaxE];
+  __shared__ int wave_tot[kGroupWaves];
+  group_block(ids, P, E, offsets, sorted, cur, wave_tot);
 }
 
 // Multi-workgroup grouping, step 1: expert counts of each segment of
@@ -512,7 +524,15 @@ static hipError_t launch_grouping(const int32_t* ids, int P, int E, int32_t* off
 
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                         int32_t* offsets, int32_t* sorted, void* ws, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, ids, w);
+  const dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, T, E, K, ids, w);
+  else if (E <= 128)
+    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, T, E, K, ids, w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, T, E, K, ids, w);
+  else
+    hipLaunchKernelGGL(topk_kernel<kMaxPerLane>, grid, block, 0, s, logits, T, E, K, ids, w);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_grouping(ids, T * K, E, offsets, sorted, ws, s);
@@ -523,8 +543,16 @@ hipError_t launch_route_scored(const float* logits, int T, int E, int K, int sig
                                int renorm, int32_t* ids, float* w, int32_t* offsets,
                                int32_t* sorted, void* ws, hipStream_t s) {
   const ScoredRouter r{sigmoid, bias, n_group, topk_group, group_top2, renorm};
-  hipLaunchKernelGGL(topk_scored_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, K, r,
-                     ids, w);
+  const dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(topk_scored_kernel<1>, grid, block, 0, s, logits, T, E, K, r, ids, w);
+  else if (E <= 128)
+    hipLaunchKernelGGL(topk_scored_kernel<2>, grid, block, 0, s, logits, T, E, K, r, ids, w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(topk_scored_kernel<4>, grid, block, 0, s, logits, T, E, K, r, ids, w);
+  else
+    hipLaunchKernelGGL(topk_scored_kernel<kMaxPerLane>, grid, block, 0, s, logits, T, E, K, r,
+                       ids, w);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_grouping(ids, T * K, E, offsets, sorted, ws, s);
