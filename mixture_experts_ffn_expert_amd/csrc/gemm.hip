@@ -827,6 +827,13 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
         read_step(b ^ 1, cur ^ 1, 0);
       }
       mfma_step(b);
+      // schedule: each MFMA followed by one LDS read of the next step, so
+      // the reads hide behind the MFMAs instead of bunching before them
+#pragma unroll
+      for (int q = 0; q < FM * FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
     }
   }
   wait_barrier<0>();  // ring free for the output staging
