@@ -45,8 +45,8 @@
  *   - A call with zero tokens (T == 0 or P == 0) returns MOE_OK and does
  *     nothing.
  *   - Limits: 1 <= K <= E, E <= 1024, K <= 32, H and I multiples of 8,
- *     T*K, T*E, T*K*I and T*K*H below 2^31 elements; the GEMM operands x,
- *     act and one expert's weight block (2I*H, H*I) below 2^30 elements.
+ *     T*K, T*E, T*K*I and T*K*H below 2^31 elements; the GEMM operands x and
+ *     act below 2^30 elements, one expert's packed weights below 2^31 bytes.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -93,6 +93,36 @@ moe_status moe_init(void);
  * not it launches (T = 0, a refused argument). Both NULL disarms; one NULL
  * is MOE_E_INVALID. Not for use under hipGraph capture. */
 moe_status moe_time_next_gemm(void* start, void* stop);
+
+typedef enum {
+  MOE_PACK_PLAIN = 0,  /* a matrix [R, K] (down projection: R = H, K = I) */
+  MOE_PACK_GATEUP = 1  /* a gate-up matrix [2I, K]: gate rows [0, I), up rows [I, 2I) */
+} moe_pack_kind;
+
+/*
+ * Packed expert weights: the weight format the grouped GEMMs read. Each
+ * expert's matrix is cut into 1 KiB blocks of 16 rows x 32 k; inside a block
+ * the 16-byte chunk q = 16*c + r holds W[16*rb + r][32*kb + 8*c .. +8], the
+ * lane order of one 16x32 MFMA operand, so every weight load of a wavefront
+ * is one contiguous 1 KiB. Rows past R and k past K are zero.
+ *   MOE_PACK_PLAIN:  block (rb, kb) at byte (rb * nkb + kb) * 1024
+ *   MOE_PACK_GATEUP: the gate block of output columns [16*cb, +16) and the
+ *                    matching up block (rows I + [16*cb, +16)) side by side:
+ *                    (cb, kb, f) at ((cb * nkb + kb) * 2 + f) * 1024, f = 0
+ *                    gate, 1 up
+ * with nkb = ceil(K / 32); experts follow one another. Packing is a layout
+ * change done once when weights are loaded, not a step of the layer (the
+ * pages' operands are the row-major W_gu [E,2I,H] and W_d [E,H,I]; the
+ * arithmetic of the GEMMs is unchanged).
+ * moe_packed_weight_bytes returns the size of the packed tensor (0 for
+ * invalid arguments: E, R, K < 1, K not a multiple of 8, R odd for GATEUP).
+ * moe_pack_weights converts w (bf16 [E, R, K], 16-byte aligned, device) into
+ * packed (device, 16-byte aligned, moe_packed_weight_bytes bytes), stream-
+ * ordered like every call. Limits: E <= 1024, R * K below 2^30 elements.
+ */
+size_t moe_packed_weight_bytes(int E, int R, int K, moe_pack_kind kind);
+moe_status moe_pack_weights(const uint16_t* w, int E, int R, int K, moe_pack_kind kind,
+                            uint16_t* packed, moe_stream_t stream);
 
 /*
  * Router / gate logits helper (not a contract step; the router itself is the
@@ -182,7 +212,9 @@ moe_status moe_route_scored(const float* logits, int T, int E, int K, moe_score 
  *   gu[j]    = bf16( f32( x[t] . w_gu[e,j] ) )          j < 2I   (N1)
  *   act[q,i] = bf16( silu(gu[i]) * gu[I+i] ),  silu(g) = g / (1 + exp(-g))
  *   x      bf16 [T,H], 16-byte aligned
- *   w_gu   bf16 [E,2I,H] (gate rows [0,I), up rows [I,2I)), 16-byte aligned
+ *   w_gu   the gate-up weights W_gu [E,2I,H] (gate rows [0,I), up rows
+ *          [I,2I)) packed by moe_pack_weights(..., E, 2I, H, MOE_PACK_GATEUP),
+ *          16-byte aligned
  *   sorted_pairs, expert_offsets  as produced by moe_route(T, E, K); both
  *          NULL means identity rows (E must be 1 and K 1: a dense expert,
  *          e.g. the shared expert)
@@ -200,7 +232,8 @@ moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const u
  *   y = f32( act[q] . w_d[e,h] );  expert_out[p,h] = bf16( y * pair_w[p] )
  *   stored at pair row p = sorted_pairs[q], so expert_out is [T,K,H].
  *   act    bf16 [P,I] in sorted order, 16-byte aligned
- *   w_d    bf16 [E,H,I], 16-byte aligned
+ *   w_d    the down weights W_d [E,H,I] packed by moe_pack_weights(..., E, H, I,
+ *          MOE_PACK_PLAIN), 16-byte aligned
  *   sorted_pairs, expert_offsets  from moe_route, or both NULL (identity, E=1)
  *   pair_w f32 [P] (= topk_w viewed flat) or NULL for no multiply
  *   expert_out bf16 [P,H], 16-byte aligned

@@ -24,7 +24,8 @@ import ctypes
 import os
 
 __all__ = [
-    "MoeError", "load", "lib_path", "moe_init", "moe_router_logits", "moe_route",
+    "MoeError", "load", "lib_path", "moe_init", "PackedWeights", "moe_pack_weights",
+    "moe_packed_weight_bytes", "moe_router_logits", "moe_route",
     "moe_route_workspace_bytes", "moe_route_scored", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
     "moe_combine_gate", "moe_layer", "moe_time_next_gemm", "MOE_F32", "MOE_BF16", "MOE_F16", "SYMBOLS",
 ]
@@ -43,6 +44,8 @@ _st = ctypes.c_int
 SYMBOLS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_init": (_st, []),
+    "moe_packed_weight_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "moe_pack_weights": (_st, [_p, _i, _i, _i, _i, _p, _p]),
     "moe_time_next_gemm": (_st, [_p, _p]),
     "moe_router_logits": (_st, [_p, _i, _i, _p, _i, _p, _p, _p]),
     "moe_route_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
@@ -240,15 +243,62 @@ def moe_route_scored(logits, K, score="softmax", selection_bias=None, n_group=1,
     return topk_ids, topk_w, expert_offsets, sorted_pairs
 
 
+MOE_PACK = {"plain": 0, "gateup": 1}
+
+
+class PackedWeights:
+    """Expert weights in the library's packed layout (``moe_pack_weights``):
+    ``data`` is the device buffer (uint8), ``E`` experts of a matrix [R, K]
+    packed as ``kind`` ("gateup": R = 2I gate and up rows; "plain")."""
+
+    def __init__(self, data, E, R, K, kind):
+        self.data, self.E, self.R, self.K, self.kind = data, E, R, K, kind
+
+    def __repr__(self):
+        return f"PackedWeights(E={self.E}, R={self.R}, K={self.K}, kind={self.kind!r})"
+
+
+def moe_packed_weight_bytes(E, R, K, kind):
+    return int(load().moe_packed_weight_bytes(E, R, K, MOE_PACK[kind]))
+
+
+def moe_pack_weights(w, kind, out=None, stream=None):
+    """Pack bf16 expert weights [E, R, K] (or [R, K], one expert) into the
+    layout the grouped GEMMs read: kind "gateup" for W_gu [E, 2I, H], "plain"
+    for W_d [E, H, I]. Done once when weights are loaded."""
+    import torch
+    if kind not in MOE_PACK:
+        raise MoeError(1, f"kind must be one of {sorted(MOE_PACK)}, got {kind!r}")
+    if w.dim() == 2:
+        w = w.unsqueeze(0)
+    _need(w, "w", torch.bfloat16, 3)
+    E, R, K = w.shape
+    nbytes = moe_packed_weight_bytes(E, R, K, kind)
+    if nbytes == 0:
+        raise MoeError(3, f"cannot pack a [{E}, {R}, {K}] matrix as {kind!r}")
+    if out is None:
+        out = torch.empty((nbytes,), dtype=torch.uint8, device=w.device)
+    _need(out, "packed", torch.uint8, shape=(nbytes,))
+    _check(load().moe_pack_weights(_ptr(w), E, R, K, MOE_PACK[kind], _ptr(out), _stream(stream)))
+    return PackedWeights(out, E, R, K, kind)
+
+
+def _need_packed(pw, name, kind, R=None, K=None):
+    if not isinstance(pw, PackedWeights):
+        raise MoeError(1, f"{name} must be PackedWeights from moe_pack_weights, got "
+                          f"{type(pw).__name__}")
+    if pw.kind != kind or (R is not None and pw.R != R) or (K is not None and pw.K != K):
+        raise MoeError(3, f"{name} is {pw!r}; expected kind={kind!r}"
+                          + (f" R={R}" if R is not None else "") + (f" K={K}" if K is not None else ""))
+
+
 def moe_grouped_gemm_gateup_silu(x, w_gu, sorted_pairs, expert_offsets, K, act=None, stream=None):
+    """w_gu: PackedWeights of W_gu [E, 2I, H] (kind "gateup")."""
     import torch
     _need(x, "x", torch.bfloat16, 2)
     T, H = x.shape
-    _need(w_gu, "w_gu", torch.bfloat16, 3)
-    E, twoI, Hw = w_gu.shape
-    if Hw != H or twoI % 2:
-        raise MoeError(3, f"w_gu must be [E, 2I, {H}], got {tuple(w_gu.shape)}")
-    I = twoI // 2
+    _need_packed(w_gu, "w_gu", "gateup", K=H)
+    E, I = w_gu.E, w_gu.R // 2
     if sorted_pairs is not None:
         _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * K,))
     if expert_offsets is not None:
@@ -256,20 +306,20 @@ def moe_grouped_gemm_gateup_silu(x, w_gu, sorted_pairs, expert_offsets, K, act=N
     if act is None:
         act = torch.empty((T * K, I), dtype=torch.bfloat16, device=x.device)
     _need(act, "act", torch.bfloat16, shape=(T * K, I))
-    _check(load().moe_grouped_gemm_gateup_silu(_ptr(x), T, H, _ptr(w_gu), E, I, _ptr(sorted_pairs),
-                                               _ptr(expert_offsets), K, _ptr(act), _stream(stream)))
+    _check(load().moe_grouped_gemm_gateup_silu(_ptr(x), T, H, _ptr(w_gu.data), E, I,
+                                               _ptr(sorted_pairs), _ptr(expert_offsets), K,
+                                               _ptr(act), _stream(stream)))
     return act
 
 
 def moe_grouped_gemm_down(act, w_d, sorted_pairs, expert_offsets, pair_w, expert_out=None,
                           stream=None):
+    """w_d: PackedWeights of W_d [E, H, I] (kind "plain")."""
     import torch
     _need(act, "act", torch.bfloat16, 2)
     P, I = act.shape
-    _need(w_d, "w_d", torch.bfloat16, 3)
-    E, H, Iw = w_d.shape
-    if Iw != I:
-        raise MoeError(3, f"w_d must be [E, H, {I}], got {tuple(w_d.shape)}")
+    _need_packed(w_d, "w_d", "plain", K=I)
+    E, H = w_d.E, w_d.R
     if sorted_pairs is not None:
         _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(P,))
     if expert_offsets is not None:
@@ -281,7 +331,7 @@ def moe_grouped_gemm_down(act, w_d, sorted_pairs, expert_offsets, pair_w, expert
     if expert_out is None:
         expert_out = torch.empty((P, H), dtype=torch.bfloat16, device=act.device)
     _need(expert_out, "expert_out", torch.bfloat16, shape=(P, H))
-    _check(load().moe_grouped_gemm_down(_ptr(act), P, I, _ptr(w_d), E, H, _ptr(sorted_pairs),
+    _check(load().moe_grouped_gemm_down(_ptr(act), P, I, _ptr(w_d.data), E, H, _ptr(sorted_pairs),
                                         _ptr(expert_offsets), _ptr(pair_w), _ptr(expert_out),
                                         _stream(stream)))
     return expert_out
@@ -325,6 +375,10 @@ def moe_layer(x, w_r, w_gu, w_d, K, router_bias=None, w_gu_s=None, w_d_s=None, w
               bufs=None, stream=None, router=None, selection_bias=None, routed_scale=1.0):
     """Enqueue one MoE layer: logits, route, gate-up, down, (shared), combine.
 
+    ``w_gu``, ``w_d`` (and ``w_gu_s``, ``w_d_s`` for a shared expert) are
+    PackedWeights from ``moe_pack_weights``; ``w_r`` and ``w_g`` are bf16
+    row-major [E, H] and [1, H].
+
     ``router`` (dict of ``moe_route_scored`` keyword arguments: score,
     n_group, topk_group, group_score, renormalize) selects the general router
     with ``selection_bias``; None routes with the ungrouped softmax top-k.
@@ -335,7 +389,7 @@ def moe_layer(x, w_r, w_gu, w_d, K, router_bias=None, w_gu_s=None, w_d_s=None, w
     import torch
     T, H = x.shape
     E = w_r.shape[0]
-    I = w_gu.shape[1] // 2
+    I = w_gu.R // 2
     b = {} if bufs is None else bufs
     dev = x.device
 
@@ -362,10 +416,10 @@ def moe_layer(x, w_r, w_gu, w_d, K, router_bias=None, w_gu_s=None, w_d_s=None, w
                                stream)
     sd = gl = None
     if w_gu_s is not None:
-        Is = w_gu_s.shape[0] // 2
-        sa = moe_grouped_gemm_gateup_silu(x, w_gu_s.view(1, 2 * Is, H), None, None, 1,
+        Is = w_gu_s.R // 2
+        sa = moe_grouped_gemm_gateup_silu(x, w_gu_s, None, None, 1,
                                           buf("sd_act", (T, Is), torch.bfloat16), stream)
-        sd = moe_grouped_gemm_down(sa, w_d_s.view(1, H, Is), None, None, None,
+        sd = moe_grouped_gemm_down(sa, w_d_s, None, None, None,
                                    buf("sd", (T, H), torch.bfloat16), stream)
         gl = moe_router_logits(x, w_g.view(1, H), None, buf("gl", (T, 1), torch.float32), stream)
     return moe_combine_gate(eo, T, K, None, routed_scale, sd, gl,

@@ -102,6 +102,11 @@ bool fits_i32(long long v) { return v >= 0 && v < (1LL << 31); }
 // block) through a buffer resource of at most 2^31 bytes: 2^30 bf16 values.
 bool fits_buf(long long elems) { return elems >= 0 && elems < (1LL << 30); }
 
+// One expert's packed weights are addressed the same way: below 2^31 bytes.
+bool fits_packed(int R, int kdim, bool gateup) {
+  return moe::packed_expert_bytes(R, kdim, gateup) < (size_t)(1u << 31);
+}
+
 // Timing armed by moe_time_next_gemm applies to one GEMM call only: every
 // GEMM entry point disarms it on return, whether or not it launched.
 struct DisarmTiming {
@@ -125,6 +130,34 @@ moe_status moe_time_next_gemm(void* start, void* stop) {
     return fail(MOE_E_INVALID, "moe_time_next_gemm: start and stop must both be set or both NULL");
   moe::set_gemm_timing(static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
   return MOE_OK;
+}
+
+size_t moe_packed_weight_bytes(int E, int R, int K, moe_pack_kind kind) {
+  if (E < 1 || R < 1 || K < 1 || K % 8 || (kind != MOE_PACK_PLAIN && kind != MOE_PACK_GATEUP))
+    return 0;
+  if (kind == MOE_PACK_GATEUP && R % 2) return 0;
+  return (size_t)E * moe::packed_expert_bytes(R, K, kind == MOE_PACK_GATEUP);
+}
+
+moe_status moe_pack_weights(const uint16_t* w, int E, int R, int K, moe_pack_kind kind,
+                            uint16_t* packed, moe_stream_t stream) {
+  const char* fn = "moe_pack_weights";
+  clear_err();
+  if (kind != MOE_PACK_PLAIN && kind != MOE_PACK_GATEUP)
+    return fail(MOE_E_INVALID, "%s: kind=%d is not MOE_PACK_PLAIN or MOE_PACK_GATEUP", fn,
+                (int)kind);
+  if (E < 1 || E > kMaxE) return fail(MOE_E_SHAPE, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if (R < 1 || (kind == MOE_PACK_GATEUP && R % 2))
+    return fail(MOE_E_SHAPE, "%s: R=%d must be positive (and even for MOE_PACK_GATEUP)", fn, R);
+  if (K < 1 || K % 8) return fail(MOE_E_SHAPE, "%s: K=%d must be a positive multiple of 8", fn, K);
+  if (!fits_packed(R, K, kind == MOE_PACK_GATEUP) || !fits_buf((long long)R * K))
+    return fail(MOE_E_SHAPE, "%s: one expert's matrix [%d, %d] is too large", fn, R, K);
+  REQUIRE_PTR(fn, w);
+  REQUIRE_PTR(fn, packed);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_pack(w, E, R, K, kind == MOE_PACK_GATEUP ? 1 : 0, packed,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
@@ -253,8 +286,8 @@ moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const u
     return fail(MOE_E_INVALID, "%s: identity rows (NULL sorted_pairs) need E=1 and K=1, got E=%d K=%d",
                 fn, E, K);
   if (!fits_i32((long long)T * K) || !fits_buf((long long)T * H) ||
-      !fits_i32((long long)T * K * I) || !fits_buf(2LL * I * H))
-    return fail(MOE_E_SHAPE, "%s: x or one expert's w_gu exceeds 2^30 elements, or T*K*I 2^31",
+      !fits_i32((long long)T * K * I) || !fits_packed(2 * I, H, true))
+    return fail(MOE_E_SHAPE, "%s: x exceeds 2^30 elements, one expert's packed w_gu 2^31 bytes, or T*K*I 2^31",
                 fn);
   if (T == 0) return MOE_OK;
   REQUIRE_PTR(fn, x);
@@ -282,8 +315,9 @@ moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const uint16
                 fn);
   if (sorted_pairs == nullptr && E != 1)
     return fail(MOE_E_INVALID, "%s: identity rows (NULL sorted_pairs) need E=1, got E=%d", fn, E);
-  if (!fits_buf((long long)P * I) || !fits_i32((long long)P * H) || !fits_buf((long long)H * I))
-    return fail(MOE_E_SHAPE, "%s: act or one expert's w_d exceeds 2^30 elements, or P*H 2^31", fn);
+  if (!fits_buf((long long)P * I) || !fits_i32((long long)P * H) || !fits_packed(H, I, false))
+    return fail(MOE_E_SHAPE,
+                "%s: act exceeds 2^30 elements, one expert's packed w_d 2^31 bytes, or P*H 2^31", fn);
   if (P == 0) return MOE_OK;
   REQUIRE_PTR(fn, act);
   REQUIRE_PTR(fn, w_d);

@@ -8,9 +8,11 @@
 // again (N3). Rows are grouped per expert (PR #523 What changed: the grouped
 // op runs over the rows' expert ids).
 //
-// Every GEMM here is C[m, n] = sum_k A[m, k] * B[n, k]: both operands are
-// k-contiguous rows (activations [rows, k], weights [E, n, k]), the friendly
-// layout for MFMA, where every lane loads 8 consecutive bf16 of one row.
+// Every GEMM here is C[m, n] = sum_k A[m, k] * B[n, k]: activations are
+// k-contiguous rows [rows, k]; expert weights W [E, n, k] arrive packed into
+// 1 KiB blocks of 16 rows x 32 k in MFMA lane order (layout below, written
+// once by pack.hip), so every weight load of a wavefront is one contiguous
+// 1 KiB; the router weights stay plain rows.
 //
 // Work decomposition. The rows of expert e are offsets[e] .. offsets[e+1]
 // of the sorted order. A "tile slot" is one BM-row block of one expert;
@@ -57,8 +59,8 @@ struct GemmArgs {
   int a_rows;               // rows of A (bounds of the gather)
   const int32_t* sorted;    // sorted pair ids, or null (row q of the problem is row q of A)
   int gather_k;             // >0: A row = sorted[q] / gather_k (gate-up); 0: A row = q
-  const uint16_t* B;        // weights [E, b_rows, kdim]
-  int b_rows;               // rows per expert in B (2I gate-up, H down, N logits)
+  const uint16_t* B;        // weights: packed blocks (gate-up, down) or [N, kdim] (logits)
+  uint32_t b_bytes;         // bytes of one expert's weights (packed or plain)
   const int32_t* offsets;   // [E+1] expert row offsets, or null (one expert, P rows)
   int E, P, kdim;
   int n_out;                // output columns (I gate-up, H down, N logits)
@@ -233,6 +235,17 @@ __device__ __forceinline__ bf16x8_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t vo
   return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// ---------------------------------------------------------------------------
+// Packed expert weights (written once by moe_pack_weights, pack.hip). One
+// expert's matrix W [R, kdim] is cut into 1 KiB blocks of 16 rows x 32 k;
+// inside a block, 16-byte chunk q = 16 c + r holds W[16 rb + r][32 kb + 8 c ..
+// + 8], the order in which the 64 lanes of a wavefront hold one 16 x 32 MFMA
+// operand, so a block is one coalesced 64-lane load. Rows past R and k past
+// kdim are zero. Down (and any plain) matrix: block (rb, kb) at
+// (rb * nkb + kb) KiB. Gate-up [2I, kdim]: the gate block of output columns
+// [16 cb, +16) and the matching up block (rows I + [16 cb, +16)) sit side by
+// side: (cb, kb, f) at ((cb * nkb + kb) * 2 + f) KiB, f = 0 gate, 1 up.
+// ---------------------------------------------------------------------------
 // Byte offset of the A row of problem row q inside A (kOob: zero row).
 __device__ __forceinline__ uint32_t a_row_off(const GemmArgs& g, int q) {
   int r = q;
@@ -245,12 +258,25 @@ __device__ __forceinline__ uint32_t a_row_off(const GemmArgs& g, int q) {
   return (uint32_t)r * (uint32_t)g.kdim * 2u;
 }
 
-// Byte offset of the weight row of output column c inside expert e's block.
-template <int EPI>
-__device__ __forceinline__ uint32_t b_row_off(const GemmArgs& g, int c, int up) {
+// Byte offset of row c of a plain (row-major) weight matrix (logits).
+__device__ __forceinline__ uint32_t b_row_off(const GemmArgs& g, int c) {
   if (c >= g.n_out) return kOob;
-  const int r = (EPI == EPI_GATEUP && up) ? g.n_out + c : c;
-  return (uint32_t)r * (uint32_t)g.kdim * 2u;
+  return (uint32_t)c * (uint32_t)g.kdim * 2u;
+}
+
+// Packed expert weights. Byte offset, at k block 0, of the 1 KiB block
+// holding output columns [16 cb, 16 cb + 16) (gate-up: gate half f = 0 or
+// up half f = 1); consecutive k blocks follow kb_stride<EPI>() bytes apart.
+template <int EPI>
+__device__ __forceinline__ uint32_t b_block_off(const GemmArgs& g, int cb, int f) {
+  if (cb * 16 >= g.n_out) return kOob;
+  const uint32_t nkb = (uint32_t)packed_nkb(g.kdim);
+  if (EPI == EPI_GATEUP) return ((uint32_t)cb * nkb * 2u + (uint32_t)f) * kPackBlock;
+  return (uint32_t)cb * nkb * kPackBlock;
+}
+template <int EPI>
+__device__ __forceinline__ constexpr uint32_t kb_stride() {
+  return EPI == EPI_GATEUP ? 2u * kPackBlock : kPackBlock;
 }
 
 // ---------------------------------------------------------------------------
@@ -278,20 +304,33 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t ra_rsrc =
       make_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
   const __amdgpu_buffer_rsrc_t rb_rsrc =
-      make_rsrc(g.B + (size_t)e * g.b_rows * g.kdim, (uint32_t)g.b_rows * (uint32_t)g.kdim * 2u);
+      make_rsrc(reinterpret_cast<const unsigned char*>(g.B) + (size_t)e * g.b_bytes, g.b_bytes);
   uint32_t va[MF];
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
     const int rr = i * 16 + r16;
     va[i] = ((rr < rows) ? a_row_off(g, row0 + rr) : kOob) + kc * 2;
   }
+  // B: plain rows for the logits (k position in the scalar offset); packed
+  // blocks for the expert weights, where lane l's 16 bytes of a 32-wide k
+  // step are the l-th chunk of one 1 KiB block
+  constexpr bool PACKED = EPI != EPI_F32;
   uint32_t vb[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f) {
     const int fo = (EPI == EPI_GATEUP) ? (f >> 1) : f;
-    const int up = (EPI == EPI_GATEUP) ? (f & 1) : 0;
-    vb[f] = b_row_off<EPI>(g, col0 + fo * 16 + r16, up) + kc * 2;
+    if constexpr (PACKED) {
+      const uint32_t o = b_block_off<EPI>(g, col0 / 16 + fo, f & 1);
+      vb[f] = (o == kOob) ? kOob : o + lane * 16;
+    } else {
+      vb[f] = b_row_off(g, col0 + fo * 16 + r16) + kc * 2;
+    }
   }
+  // scalar B offset of the 32-wide k step starting at k
+  auto bsoff = [&](int k) -> uint32_t {
+    if constexpr (PACKED) return (uint32_t)(k >> 5) * kb_stride<EPI>();
+    return (uint32_t)k * 2u;
+  };
   f32x4_t acc[MF][NB];
 #pragma unroll
   for (int i = 0; i < MF; ++i)
@@ -309,8 +348,9 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(GemmArgs g) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t soff = (uint32_t)(k0 + u * 32) * 2u;
+      const uint32_t sb = bsoff(k0 + u * 32);
 #pragma unroll
-      for (int f = 0; f < NB; ++f) b[u][f] = bload8(rb_rsrc, vb[f], soff);
+      for (int f = 0; f < NB; ++f) b[u][f] = bload8(rb_rsrc, vb[f], sb);
 #pragma unroll
       for (int i = 0; i < MF; ++i) a[u][i] = bload8(ra_rsrc, va[i], soff);
     }
@@ -327,7 +367,7 @@ __global__ __launch_bounds__(64 * KS) void stream_kernel(GemmArgs g) {
     const uint32_t soff = (uint32_t)k0 * 2u;
     bf16x8_t a[MF], b[NB];
 #pragma unroll
-    for (int f = 0; f < NB; ++f) b[f] = bload8(rb_rsrc, in ? vb[f] : kOob, soff);
+    for (int f = 0; f < NB; ++f) b[f] = bload8(rb_rsrc, in ? vb[f] : kOob, bsoff(k0));
 #pragma unroll
     for (int i = 0; i < MF; ++i) a[i] = bload8(ra_rsrc, in ? va[i] : kOob, soff);
 #pragma unroll
@@ -450,7 +490,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t ra_rsrc =
       make_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
   const __amdgpu_buffer_rsrc_t rb_rsrc =
-      make_rsrc(g.B + (size_t)e * g.b_rows * g.kdim, (uint32_t)g.b_rows * (uint32_t)g.kdim * 2u);
+      make_rsrc(reinterpret_cast<const unsigned char*>(g.B) + (size_t)e * g.b_bytes, g.b_bytes);
   uint32_t va[A_CH], vb[B_CH];  // per-thread byte offsets (k = 0)
   int sa[A_CH], sb[B_CH];       // LDS element offsets
   int ca[A_CH], cb[B_CH];       // k offset (elements) of the chunk within the step
@@ -462,20 +502,29 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
     sa[i] = r * LD + c * 8;
     ca[i] = c * 8;
   }
+  // B (packed weights): consecutive threads take consecutive 16-byte chunks
+  // of one packed block (block bi: tile rows [16 (bi / KBS), +16), k block
+  // bi % KBS of the step; chunk q: k chunk q / 16 of row q % 16)
+  constexpr int KBS = BK / 32;
+  static_assert(BK % 32 == 0, "packed k blocks per step");
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int ci = tid + NT * i, r = ci / CPR, c = ci % CPR;
-    int col, up = 0;
+    const int ci = tid + NT * i, bi = ci / 64, q = ci % 64;
+    const int tb = bi / KBS, kb = bi % KBS;
+    const int r = tb * 16 + (q & 15), c = kb * 4 + (q >> 4);  // tile row, 16-byte k chunk
+    int colb, f = 0;  // packed column block and gate / up half
     if (EPI == EPI_GATEUP) {
       // wave column wn owns TN weight rows: fragment pairs (gate, up) of
       // 32 output columns each
-      const int wn = r / TN, f = (r % TN) >> 5, j = r & 31;
-      col = n0 + wn * (TN / 2) + (f >> 1) * 32 + j;
-      up = f & 1;
+      const int br = tb * 16;
+      const int wn = br / TN, fl = (br % TN) >> 5, j = br & 31;
+      colb = (n0 + wn * (TN / 2) + (fl >> 1) * 32 + j) / 16;
+      f = fl & 1;
     } else {
-      col = n0 + r;
+      colb = (n0 + tb * 16) / 16;
     }
-    vb[i] = b_row_off<EPI>(g, col, up) + c * 16;
+    const uint32_t o = b_block_off<EPI>(g, colb, f);
+    vb[i] = (o == kOob) ? kOob : o + (uint32_t)kb * kb_stride<EPI>() + q * 16;
     sb[i] = r * LD + c * 8;
     cb[i] = c * 8;
   }
@@ -485,18 +534,19 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
   bf16x8_t ra[PF][A_CH], rb[PF][B_CH];
   auto gload = [&](int st, int k0) {
     const uint32_t soff = (uint32_t)k0 * 2u;
+    const uint32_t soff_b = (uint32_t)(k0 / 32) * kb_stride<EPI>();
     if (k0 + BK <= g.kdim) {
 #pragma unroll
       for (int i = 0; i < A_CH; ++i) ra[st][i] = bload8(ra_rsrc, va[i], soff);
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) rb[st][i] = bload8(rb_rsrc, vb[i], soff);
+      for (int i = 0; i < B_CH; ++i) rb[st][i] = bload8(rb_rsrc, vb[i], soff_b);
     } else {  // last, partial k step: chunks at or past kdim read as zero
 #pragma unroll
       for (int i = 0; i < A_CH; ++i)
         ra[st][i] = bload8(ra_rsrc, (k0 + ca[i] < g.kdim) ? va[i] : kOob, soff);
 #pragma unroll
       for (int i = 0; i < B_CH; ++i)
-        rb[st][i] = bload8(rb_rsrc, (k0 + cb[i] < g.kdim) ? vb[i] : kOob, soff);
+        rb[st][i] = bload8(rb_rsrc, (k0 + cb[i] < g.kdim) ? vb[i] : kOob, soff_b);
     }
   };
   auto sstore = [&](int st) {
@@ -613,10 +663,12 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
 // multiplied, with no register staging; the MFMA operands of the next 16-wide
 // k step are read from LDS while the current step's MFMAs run, and the one
 // barrier per stage sits before the last k step of the stage, so the reads of
-// the next stage's first step overlap that step's MFMAs. LDS rows are 2*BK bytes,
-// unpadded; 16-byte chunk c of tile row r sits in slot c ^ ((r >> 1) & (BK/8 -
-// 1)), which keeps the 16-byte fragment reads of 8 consecutive rows on
-// distinct banks.
+// the next stage's first step overlap that step's MFMAs. A (activation rows):
+// LDS rows of 2*BK bytes, unpadded; 16-byte chunk c of tile row r sits in
+// slot c ^ ((r >> 1) & (BK/8 - 1)), which keeps the 16-byte fragment reads of
+// 8 consecutive rows on distinct banks. B (packed weights): the packed 1 KiB
+// blocks as they come, where a fragment read of 16 rows is 256 contiguous
+// bytes.
 //
 // The loads are issued from inline assembly and the waits are explicit
 // (s_waitcnt vmcnt(N) lgkmcnt(0); s_barrier): the compiler cannot tell which
@@ -719,44 +771,53 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
 
   const i32x4_t rsrc_a = raw_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
   const i32x4_t rsrc_b =
-      raw_rsrc(g.B + (size_t)e * g.b_rows * g.kdim, (uint32_t)g.b_rows * (uint32_t)g.kdim * 2u);
-  // Load j of this wave fills tile rows [RPL*(wave*IPW + j), +RPL) of a ring
-  // slot: lane l writes slot (l%CPR) of row l/CPR, i.e. logical chunk
-  // (l%CPR) ^ swz(row).
+      raw_rsrc(reinterpret_cast<const unsigned char*>(g.B) + (size_t)e * g.b_bytes, g.b_bytes);
+  // A: load j of this wave fills tile rows [RPL*(wave*IPW + j), +RPL) of a
+  // ring slot: lane l writes slot (l%CPR) of row l/CPR, i.e. logical chunk
+  // (l%CPR) ^ swz(row). B (packed weights): each 1 KiB load copies one packed
+  // block; B load b holds tile rows [16 (b / KBS), +16) at k block b % KBS.
+  constexpr int KBS = BK / 32;  // packed k blocks per stage
   uint32_t voff[IPW];
   int chunk[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
-    const int r = (wave * IPW + j) * RPL + lane / CPR;  // tile row (A rows, then B rows)
-    const int c = (lane % CPR) ^ ((r >> 1) & (CPR - 1));
-    uint32_t ro;
-    if (r < BM) {
-      ro = (r < rows) ? a_row_off(g, row0 + r) : kOob;
+    const int blk = wave * IPW + j;
+    if (blk * RPL < BM) {
+      const int r = blk * RPL + lane / CPR;
+      const int c = (lane % CPR) ^ ((r >> 1) & (CPR - 1));
+      voff[j] = ((r < rows) ? a_row_off(g, row0 + r) : kOob) + c * 16;
+      chunk[j] = c * 8;
     } else {
-      const int br = r - BM;
-      int col, up = 0;
+      const int bl = blk - BM / RPL;
+      const int tb = bl / KBS, kb = bl % KBS;
+      const int br = tb * 16;  // first tile row of the block
+      int cb, f = 0;
       if (EPI == EPI_GATEUP) {
-        const int wn = br / TN, f = (br % TN) >> 5, jj = br & 31;
-        col = n0 + wn * (TN / 2) + (f >> 1) * 32 + jj;
-        up = f & 1;
+        const int wn = br / TN, fl = (br % TN) >> 5, jj = br & 31;
+        cb = (n0 + wn * (TN / 2) + (fl >> 1) * 32 + jj) / 16;
+        f = fl & 1;
       } else {
-        col = n0 + br;
+        cb = (n0 + br) / 16;
       }
-      ro = b_row_off<EPI>(g, col, up);
+      const uint32_t o = b_block_off<EPI>(g, cb, f);
+      voff[j] = (o == kOob) ? kOob : o + (uint32_t)kb * kb_stride<EPI>() + lane * 16;
+      chunk[j] = kb * 32 + (lane >> 4) * 8;
     }
-    voff[j] = ro + c * 16;
-    chunk[j] = c * 8;
   }
   const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_addr(ring));
   auto issue = [&](int slot, int k0) {
-    const uint32_t soff = (uint32_t)k0 * 2u;
+    const uint32_t soff_a = (uint32_t)k0 * 2u;
+    const uint32_t soff_b = (uint32_t)(k0 / 32) * kb_stride<EPI>();
     const bool full = k0 + BK <= g.kdim;
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int blk = wave * IPW + j;  // uniform
       const uint32_t m0 = ring_base + slot * STAGE + blk * 1024;
       const uint32_t vo = (full || k0 + chunk[j] < g.kdim) ? voff[j] : kOob;
-      dma16(blk * RPL < BM ? rsrc_a : rsrc_b, m0, vo, soff);
+      if (blk * RPL < BM)
+        dma16(rsrc_a, m0, vo, soff_a);
+      else
+        dma16(rsrc_b, m0, vo, soff_b);
     }
   };
 
@@ -781,10 +842,13 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   }
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
-    const int r = BM + wn * TN + f * 32 + r32;
+    const int br = wn * TN + f * 32 + r32;  // tile row of B
+    const int tb = br >> 4, rr = br & 15;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk)
-      boff[f][kk] = r * ROWB + (((kk * 2 + khalf) ^ ((r >> 1) & (CPR - 1))) * 16);
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int kb = kk >> 1, c = (kk & 1) * 2 + khalf;
+      boff[f][kk] = BM * ROWB + (tb * KBS + kb) * 1024 + (c * 16 + rr) * 16;
+    }
   }
   // MFMA operands of one 16-wide k step, double-buffered across steps
   constexpr int KK = BK / 16;
@@ -948,14 +1012,14 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
     if (avg_rows <= 24.0 || tiled_blocks < 512) {
       if (avg_rows <= 8.0) {
         // decode-like: 16-row tiles of 16 columns; gate-up (gate + up
-        // fragments) splits k over 4 waves with 8 k steps in flight per
-        // wave, down splits k over 3 waves with 2 in flight
+        // fragments) splits k over 8 waves with 4 k steps in flight per
+        // wave, down splits k over 3 waves with 4 in flight
         g.slots = slots_for(g.P, g.E, 16, grouped);
         g.nblk = (g.n_out + 15) / 16;
         if constexpr (EPI == EPI_GATEUP)
-          return run(stream_kernel<EPI, 1, 1, 4, 8>, grid_for(g), 256, s, g);
+          return run(stream_kernel<EPI, 1, 1, 8, 4>, grid_for(g), 512, s, g);
         else
-          return run(stream_kernel<EPI, 1, 1, 3, 2>, grid_for(g), 192, s, g);
+          return run(stream_kernel<EPI, 1, 1, 3, 4>, grid_for(g), 192, s, g);
       }
       // tens of rows per tile: 32-row tiles; gate-up 64 columns (routed)
       // or 32 (dense), down 32 columns, k split over 4 waves
@@ -998,7 +1062,7 @@ hipError_t launch_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w
   g.sorted = sorted;
   g.gather_k = K;
   g.B = w_gu;
-  g.b_rows = 2 * I;
+  g.b_bytes = (uint32_t)packed_expert_bytes(2 * I, H, true);
   g.offsets = offsets;
   g.E = E;
   g.P = T * K;
@@ -1017,7 +1081,7 @@ hipError_t launch_down(const uint16_t* act, int P, int I, const uint16_t* w_d, i
   g.sorted = sorted;
   g.gather_k = 0;  // act is already in sorted order: row q of the problem is row q of act
   g.B = w_d;
-  g.b_rows = H;
+  g.b_bytes = (uint32_t)packed_expert_bytes(H, I, false);
   g.offsets = offsets;
   g.E = E;
   g.P = P;
@@ -1036,7 +1100,7 @@ hipError_t launch_logits(const uint16_t* x, int T, int H, const uint16_t* w, int
   g.sorted = nullptr;
   g.gather_k = 0;
   g.B = w;
-  g.b_rows = N;
+  g.b_bytes = (uint32_t)((size_t)N * H * 2);
   g.offsets = nullptr;
   g.E = 1;
   g.P = T;

@@ -7,6 +7,21 @@
 
 namespace moe {
 
+// Packed expert weights: 1 KiB blocks of 16 rows x 32 k (layout in gemm.hip).
+constexpr uint32_t kPackBlock = 1024;
+__host__ __device__ inline int packed_nkb(int kdim) { return (kdim + 31) / 32; }
+// Bytes of one expert's packed matrix: gate-up [2I, kdim] (R = 2I) or plain
+// [R, kdim].
+__host__ __device__ inline size_t packed_expert_bytes(int R, int kdim, bool gateup) {
+  const size_t nkb = (size_t)packed_nkb(kdim);
+  if (gateup) return (size_t)((R / 2 + 15) / 16) * nkb * 2 * kPackBlock;
+  return (size_t)((R + 15) / 16) * nkb * kPackBlock;
+}
+
+// pack.hip
+hipError_t launch_pack(const uint16_t* w, int E, int R, int kdim, int gateup, uint16_t* out,
+                       hipStream_t s);
+
 // route.hip
 size_t route_workspace_bytes(int T, int E, int K);
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w,

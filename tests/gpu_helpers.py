@@ -20,6 +20,18 @@ def to_dev_bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16)).view(torch.bfloat16).to(DEV)
 
 
+def packed_gu(w):
+    """Gate-up weights (bf16 bits [E, 2I, H] or [2I, H]) packed on the GPU."""
+    import mixture_experts_ffn_expert_amd as moe
+    return moe.moe_pack_weights(to_dev_bf16(w), "gateup")
+
+
+def packed_d(w):
+    """Down weights (bf16 bits [E, H, I] or [H, I]) packed on the GPU."""
+    import mixture_experts_ffn_expert_amd as moe
+    return moe.moe_pack_weights(to_dev_bf16(w), "plain")
+
+
 def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 

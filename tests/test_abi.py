@@ -191,3 +191,22 @@ def test_route_scored_refusals(lib, E, K, score, n_group, topk_group, gscore, re
     st = lib.moe_route_scored(A, 4, E, K, score, None, n_group, topk_group, gscore, renorm,
                               A, A, A, A, None, 0, None)
     assert st == status and word in _err(lib) and "moe_route_scored" in _err(lib)
+
+
+def test_packed_weight_bytes(lib):
+    # 1 KiB blocks of 16 rows x 32 k; gate-up pairs gate and up blocks
+    assert lib.moe_packed_weight_bytes(128, 2048, 768, 0) == 128 * 128 * 24 * 1024
+    assert lib.moe_packed_weight_bytes(128, 1536, 2048, 1) == 128 * 48 * 64 * 2 * 1024
+    assert lib.moe_packed_weight_bytes(2, 40, 72, 0) == 2 * 3 * 3 * 1024
+    assert lib.moe_packed_weight_bytes(1, 80, 136, 1) == 1 * 3 * 5 * 2 * 1024
+    assert lib.moe_packed_weight_bytes(1, 81, 136, 1) == 0       # odd R for gate-up
+    assert lib.moe_packed_weight_bytes(1, 80, 12, 0) == 0        # K not a multiple of 8
+    assert lib.moe_packed_weight_bytes(0, 80, 16, 0) == 0
+
+
+def test_pack_refusals(lib):
+    assert lib.moe_pack_weights(A, 2, 40, 12, 0, A2, None) == 3 and "K=12" in _err(lib)
+    assert lib.moe_pack_weights(A, 2, 41, 16, 1, A2, None) == 3 and "even" in _err(lib)
+    assert lib.moe_pack_weights(A, 2, 40, 16, 2, A2, None) == 1 and "kind" in _err(lib)
+    assert lib.moe_pack_weights(MIS, 2, 40, 16, 0, A2, None) == 1 and "aligned" in _err(lib)
+    assert lib.moe_pack_weights(A, 2, 40, 16, 0, None, None) == 1 and "packed" in _err(lib)

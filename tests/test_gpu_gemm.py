@@ -21,8 +21,8 @@ import torch
 import oracle as O
 import workloads as W
 from conftest import cached_inputs
-from gpu_helpers import (DEV, assert_bits_equal, assert_gemm_close, bits, sample_rows, sub_down,
-                         sub_gateup, to_dev, to_dev_bf16)
+from gpu_helpers import (DEV, assert_bits_equal, assert_gemm_close, bits, packed_d, packed_gu,
+                         sample_rows, sub_down, sub_gateup, to_dev, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
@@ -66,7 +66,7 @@ def test_gemms_bit_exact_on_exact_arithmetic(gpu_lib, T, H, E, K, I, skew):
     ids, w, off, sp = _routing_for(T, E, K, seed + 2, skew)
     if skew:
         assert np.any(np.diff(off) == 0), "expected empty experts"
-    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), to_dev_bf16(wgu), to_dev(sp),
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), packed_gu(wgu), to_dev(sp),
                                                to_dev(off), K)
     torch.cuda.synchronize()
     ref_act = O.gateup_silu(x, wgu, sp, off, K)
@@ -74,11 +74,11 @@ def test_gemms_bit_exact_on_exact_arithmetic(gpu_lib, T, H, E, K, I, skew):
     # down on an exact act (its own values) so the sums stay exact
     a2 = _exact_bf16(seed + 3, (T * K, I), -8, 8, 2.0 ** -4)
     wd = _exact_bf16(seed + 4, (E, H, I), -4, 4, 2.0 ** -5)
-    eo = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), to_dev_bf16(wd), to_dev(sp), to_dev(off),
+    eo = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), packed_d(wd), to_dev(sp), to_dev(off),
                                        to_dev(w.reshape(-1)))
     torch.cuda.synchronize()
     assert_bits_equal(bits(eo), O.down_proj(a2, wd, sp, off, w.reshape(-1)), "expert_out")
-    eo0 = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), to_dev_bf16(wd), to_dev(sp), to_dev(off),
+    eo0 = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), packed_d(wd), to_dev(sp), to_dev(off),
                                         None)
     torch.cuda.synchronize()
     assert_bits_equal(bits(eo0), O.down_proj(a2, wd, sp, off, None), "expert_out unweighted")
@@ -95,13 +95,13 @@ def test_tiled_gemms_bit_exact_on_exact_arithmetic(gpu_lib, skew):
     x = _exact_bf16(seed, (T, H), -4, 4, 1.0)
     wgu = _exact_bf16(seed + 1, (E, 2 * I, H), -4, 4, 2.0 ** -6)
     ids, w, off, sp = _routing_for(T, E, K, seed + 2, skew)
-    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), to_dev_bf16(wgu), to_dev(sp),
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), packed_gu(wgu), to_dev(sp),
                                                to_dev(off), K)
     torch.cuda.synchronize()
     assert_bits_equal(bits(act), O.gateup_silu(x, wgu, sp, off, K), "act")
     a2 = _exact_bf16(seed + 3, (T * K, I), -8, 8, 2.0 ** -4)
     wd = _exact_bf16(seed + 4, (E, H, I), -4, 4, 2.0 ** -5)
-    eo = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), to_dev_bf16(wd), to_dev(sp), to_dev(off),
+    eo = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), packed_d(wd), to_dev(sp), to_dev(off),
                                        to_dev(w.reshape(-1)))
     torch.cuda.synchronize()
     assert_bits_equal(bits(eo), O.down_proj(a2, wd, sp, off, w.reshape(-1)), "expert_out")
@@ -112,10 +112,10 @@ def test_identity_rows_bit_exact(gpu_lib, T, H, I):
     """NULL sorted_pairs/offsets: a dense expert (the shared expert)."""
     x = _exact_bf16(T + H, (T, H), -4, 4, 1.0)
     wgu = _exact_bf16(I + 1, (1, 2 * I, H), -4, 4, 2.0 ** -6)
-    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), to_dev_bf16(wgu), None, None, 1)
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), packed_gu(wgu), None, None, 1)
     a2 = _exact_bf16(I + 2, (T, I), -8, 8, 2.0 ** -4)
     wd = _exact_bf16(I + 3, (1, H, I), -4, 4, 2.0 ** -5)
-    sd = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), to_dev_bf16(wd), None, None, None)
+    sd = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(a2), packed_d(wd), None, None, None)
     torch.cuda.synchronize()
     assert_bits_equal(bits(act), O.gateup_silu(x, wgu, None, None, 1), "shared act")
     assert_bits_equal(bits(sd), O.down_proj(a2, wd, None, None, None), "shared down")
@@ -140,7 +140,7 @@ def test_gateup_golden_on_gpu(gpu_lib, case):
     wgu = np.zeros((E, 2 * Ip, Hp), F32)
     wgu[:, :I, :H] = wg[:, :I]
     wgu[:, Ip:Ip + I, :H] = wg[:, I:]
-    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), to_dev_bf16(O.bf16_from_f32(wgu)),
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), packed_gu(O.bf16_from_f32(wgu)),
                                                to_dev(np.array(case["sorted_pairs"], np.int32)),
                                                to_dev(np.array(case["offsets"], np.int32)), K)
     torch.cuda.synchronize()
@@ -154,7 +154,7 @@ def test_down_golden_on_gpu(gpu_lib, case):
     Ip, Hp = 8, 8
     act = O.bf16_from_f32(_pad(np.array(case["act"], F32), (P, Ip)))
     wd = O.bf16_from_f32(_pad(np.array(case["w_d"], F32), (E, Hp, Ip)))
-    eo = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(act), to_dev_bf16(wd),
+    eo = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(act), packed_d(wd),
                                        to_dev(np.array(case["sorted_pairs"], np.int32)),
                                        to_dev(np.array(case["offsets"], np.int32)),
                                        to_dev(np.array(case["pair_w"], F32)))
@@ -170,7 +170,7 @@ def test_gemms_stagewise_workloads(gpu_lib, n):
     print(f"stagewise gemm cfg={n} T={cfg.T}", flush=True)
     logits = O.router_logits(d["x"], d["w_r"], d.get("router_bias"))
     ids, w, off, sp = O.route(logits, cfg.K)
-    x_d, wgu_d, wd_d = to_dev_bf16(d["x"]), to_dev_bf16(d["w_gu"]), to_dev_bf16(d["w_d"])
+    x_d, wgu_d, wd_d = to_dev_bf16(d["x"]), packed_gu(d["w_gu"]), packed_d(d["w_d"])
     act = gpu_lib.moe_grouped_gemm_gateup_silu(x_d, wgu_d, to_dev(sp), to_dev(off), cfg.K)
     torch.cuda.synchronize()
     ref_act = O.gateup_silu(d["x"], d["w_gu"], sp, off, cfg.K)
@@ -182,11 +182,11 @@ def test_gemms_stagewise_workloads(gpu_lib, n):
     assert_gemm_close(bits(eo), O.down_proj(ref_act, d["w_d"], sp, off, w.reshape(-1)),
                       f"cfg{n} expert_out")
     if "w_gu_s" in d:
-        sa = gpu_lib.moe_grouped_gemm_gateup_silu(x_d, to_dev_bf16(d["w_gu_s"][None]), None, None, 1)
+        sa = gpu_lib.moe_grouped_gemm_gateup_silu(x_d, packed_gu(d["w_gu_s"][None]), None, None, 1)
         torch.cuda.synchronize()
         ref_sa = O.gateup_silu(d["x"], d["w_gu_s"][None], None, None, 1)
         assert_gemm_close(bits(sa), ref_sa, f"cfg{n} shared act")
-        sd = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(ref_sa), to_dev_bf16(d["w_d_s"][None]),
+        sd = gpu_lib.moe_grouped_gemm_down(to_dev_bf16(ref_sa), packed_d(d["w_d_s"][None]),
                                            None, None, None)
         torch.cuda.synchronize()
         assert_gemm_close(bits(sd), O.down_proj(ref_sa, d["w_d_s"][None], None, None, None),
@@ -200,9 +200,9 @@ def test_gemms_skewed_full_size_sampled(gpu_lib):
     logits = O.router_logits(d["x"], d["w_r"], d["router_bias"])
     ids, w, off, sp = O.route(logits, cfg.K)
     assert np.count_nonzero(np.diff(off) == 0) > 0, "skewed routing leaves experts empty"
-    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(d["x"]), to_dev_bf16(d["w_gu"]),
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(d["x"]), packed_gu(d["w_gu"]),
                                                to_dev(sp), to_dev(off), cfg.K)
-    eo = gpu_lib.moe_grouped_gemm_down(act, to_dev_bf16(d["w_d"]), to_dev(sp), to_dev(off),
+    eo = gpu_lib.moe_grouped_gemm_down(act, packed_d(d["w_d"]), to_dev(sp), to_dev(off),
                                        to_dev(w.reshape(-1)))
     torch.cuda.synchronize()
     qs = sample_rows(off, 3, seed=5)
@@ -238,7 +238,7 @@ def test_gemm_output_canaries(gpu_lib):
     ids, w, off, sp = _routing_for(T, E, K, 3)
     full = torch.full((T * K * I + 256,), 0x7BCD, dtype=torch.int16, device=DEV)
     act = full[: T * K * I].view(torch.bfloat16).view(T * K, I)
-    gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), to_dev_bf16(wgu), to_dev(sp), to_dev(off),
+    gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), packed_gu(wgu), to_dev(sp), to_dev(off),
                                          K, act=act)
     torch.cuda.synchronize()
     assert torch.all(full[T * K * I:] == 0x7BCD).item(), "gate-up wrote past act"
@@ -253,7 +253,7 @@ def test_timed_gemm_launch_matches_untimed(gpu_lib):
     wgu = W.random_bf16(12, (E, 2 * I, H), 1.0 / np.sqrt(H))
     wd = W.random_bf16(13, (E, H, I), 1.0 / np.sqrt(I))
     ids, w, off, sp = _routing_for(T, E, K, 14)
-    x_d, wgu_d, wd_d, sp_d, off_d = (to_dev_bf16(x), to_dev_bf16(wgu), to_dev_bf16(wd),
+    x_d, wgu_d, wd_d, sp_d, off_d = (to_dev_bf16(x), packed_gu(wgu), packed_d(wd),
                                      to_dev(sp), to_dev(off))
     pw = to_dev(w.reshape(-1))
     ref_act = gpu_lib.moe_grouped_gemm_gateup_silu(x_d, wgu_d, sp_d, off_d, K)

@@ -21,8 +21,8 @@ import torch
 import oracle as O
 import workloads as W
 from conftest import cached_inputs
-from gpu_helpers import (DEV, assert_bits_equal, assert_gemm_close, bits, sample_rows, sub_down,
-                         sub_gateup, to_dev_bf16)
+from gpu_helpers import (DEV, assert_bits_equal, assert_gemm_close, bits, packed_d, packed_gu,
+                         sample_rows, sub_down, sub_gateup, to_dev_bf16)
 
 import mixture_experts_ffn_expert_amd as moe
 
@@ -30,7 +30,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _dev_inputs(d):
-    t = {k: to_dev_bf16(d[k]) for k in ("x", "w_r", "w_gu", "w_d")}
+    t = {k: to_dev_bf16(d[k]) for k in ("x", "w_r")}
+    t["w_gu"], t["w_d"] = packed_gu(d["w_gu"]), packed_d(d["w_d"])
     t["router_bias"] = None
     if "router_bias" in d:
         t["router_bias"] = torch.from_numpy(d["router_bias"]).to(DEV)
@@ -38,8 +39,9 @@ def _dev_inputs(d):
     if "selection_bias" in d:
         t["selection_bias"] = torch.from_numpy(d["selection_bias"]).to(DEV)
     t["router"] = W.router_args(d["cfg"])
-    for k in ("w_gu_s", "w_d_s", "w_g"):
-        t[k] = to_dev_bf16(d[k]) if k in d else None
+    t["w_gu_s"] = packed_gu(d["w_gu_s"]) if "w_gu_s" in d else None
+    t["w_d_s"] = packed_d(d["w_d_s"]) if "w_d_s" in d else None
+    t["w_g"] = to_dev_bf16(d["w_g"]) if "w_g" in d else None
     return t
 
 
