@@ -12,4 +12,8 @@ brute-force dense evaluation). The GEMM values have no external printed
 reference, so those are pinned only by the self-built checks listed there.
 """
 from .moe_oracle import *  # noqa: F401,F403
-from .moe_oracle import __all__  # noqa: F401
+from .keepquant import *  # noqa: F401,F403
+from . import keepquant as _kq
+from . import moe_oracle as _mo
+
+__all__ = list(_mo.__all__) + list(_kq.__all__)
