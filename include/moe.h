@@ -264,6 +264,56 @@ moe_status moe_combine_gate(const void* expert_out, moe_dtype eo_dt, int T, int 
                             moe_dtype sh_dt, const float* gate_logit, void* out,
                             moe_dtype out_dt, moe_stream_t stream);
 
+/*
+ * Keep-quant grouped expert GEMMs ([PR 523] What changed: expert weights stay
+ * in their GGUF block format, activations are quantized on the fly, dot
+ * products run per super-block with an integer core). Weight type: GGUF Q4_K
+ * (type number 12): per 256 weights, 144 bytes = f16 d, f16 dmin, 12 bytes of
+ * six-bit sub-block scales and mins, 128 bytes of 4-bit quants; a weight
+ * matrix [R, K] is R rows of K/256 such blocks, experts one after another.
+ * Activations: Q8_K (per 256 values: scale d, 256 int8 quants, sums of 16).
+ * Per super-block the dot product of a weight row and an activation row is
+ *   d_w d_x sum_j sc_j (sum_{l in j} q4_l q8_l) - dmin_w d_x sum_j m_j bsum_j
+ * (integer inside, one f32 step per super-block, f32 sum over super-blocks).
+ */
+typedef enum { MOE_Q4_K = 12 } moe_qtype;
+
+/* Bytes of the Q8_K buffer of R rows of K values (K a positive multiple of
+ * 256; 0 otherwise or for R = 0). Layout, each section 256-byte aligned:
+ * int8 quants [R, K], then f32 scales [R, K/256], then int32 sums of 16
+ * quants [R, K/16]. */
+size_t moe_q8k_bytes(int R, int K);
+
+/* Q8_K quantization of bf16 rows x [R, K] (16-byte aligned) into xq
+ * (moe_q8k_bytes(R, K) bytes, 16-byte aligned): per 256 values, the first
+ * entry of largest magnitude gives iscale = -127 / max, q = min(127,
+ * round-half-even(iscale * x)), d = 1 / iscale (f32); an all-zero block gives
+ * d = 0, q = 0. Activations must be finite. */
+moe_status moe_quantize_q8k(const uint16_t* x, int R, int K, void* xq, moe_stream_t stream);
+
+/* Keep-quant grouped gate-up with SiLU-mul ([PR 523]; [Issue 3094] N1):
+ *   g, u = keep-quant dots of the Q8_K row of token t = sorted_pairs[q] / K
+ *          with gate row c and up row I + c of expert e (Q4_K w_gu [E, 2I, H])
+ *   act[q, c] = bf16(silu(bf16(g)) * bf16(u))
+ * xq: moe_quantize_q8k of x [T, H]; H a multiple of 256; routing arguments,
+ * act and errors as moe_grouped_gemm_gateup_silu; wt must be MOE_Q4_K
+ * (MOE_E_DTYPE otherwise). */
+moe_status moe_grouped_qgemm_gateup_silu(const void* xq, int T, int H, const void* w_gu,
+                                         moe_qtype wt, int E, int I, const int32_t* sorted_pairs,
+                                         const int32_t* expert_offsets, int K, uint16_t* act,
+                                         moe_stream_t stream);
+
+/* Keep-quant grouped down projection ([PR 523]; [Issue 3094] N2, N3):
+ *   y = keep-quant dot of the Q8_K row q of act with row h of expert e's
+ *       Q4_K w_d [E, H, I];  expert_out[p, h] = bf16(y * pair_w[p]), p =
+ *       sorted_pairs[q]
+ * actq: moe_quantize_q8k of act [P, I]; I a multiple of 256; the rest as
+ * moe_grouped_gemm_down. */
+moe_status moe_grouped_qgemm_down(const void* actq, int P, int I, const void* w_d, moe_qtype wt,
+                                  int E, int H, const int32_t* sorted_pairs,
+                                  const int32_t* expert_offsets, const float* pair_w,
+                                  uint16_t* expert_out, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,8 @@ import os
 
 __all__ = [
     "MoeError", "load", "lib_path", "moe_init", "PackedWeights", "moe_pack_weights",
-    "moe_packed_weight_bytes", "moe_router_logits", "moe_route",
+    "moe_packed_weight_bytes", "Q8KBuffer", "moe_q8k_bytes", "moe_quantize_q8k",
+    "moe_grouped_qgemm_gateup_silu", "moe_grouped_qgemm_down", "MOE_Q4_K", "moe_router_logits", "moe_route",
     "moe_route_workspace_bytes", "moe_route_scored", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
     "moe_combine_gate", "moe_layer", "moe_time_next_gemm", "MOE_F32", "MOE_BF16", "MOE_F16", "SYMBOLS",
 ]
@@ -45,6 +46,10 @@ SYMBOLS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_init": (_st, []),
     "moe_packed_weight_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "moe_q8k_bytes": (ctypes.c_size_t, [_i, _i]),
+    "moe_quantize_q8k": (_st, [_p, _i, _i, _p, _p]),
+    "moe_grouped_qgemm_gateup_silu": (_st, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _i, _p, _p]),
+    "moe_grouped_qgemm_down": (_st, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _p, _p, _p]),
     "moe_pack_weights": (_st, [_p, _i, _i, _i, _i, _p, _p]),
     "moe_time_next_gemm": (_st, [_p, _p]),
     "moe_router_logits": (_st, [_p, _i, _i, _p, _i, _p, _p, _p]),
@@ -334,6 +339,89 @@ def moe_grouped_gemm_down(act, w_d, sorted_pairs, expert_offsets, pair_w, expert
     _check(load().moe_grouped_gemm_down(_ptr(act), P, I, _ptr(w_d.data), E, H, _ptr(sorted_pairs),
                                         _ptr(expert_offsets), _ptr(pair_w), _ptr(expert_out),
                                         _stream(stream)))
+    return expert_out
+
+
+MOE_Q4_K = 12
+Q4K_BLOCK = 144
+
+
+class Q8KBuffer:
+    """Q8_K-quantized activations (``moe_quantize_q8k``): ``data`` (uint8,
+    moe_q8k_bytes(R, K) bytes) for R rows of K values."""
+
+    def __init__(self, data, R, K):
+        self.data, self.R, self.K = data, R, K
+
+
+def moe_q8k_bytes(R, K):
+    return int(load().moe_q8k_bytes(R, K))
+
+
+def moe_quantize_q8k(x, out=None, stream=None):
+    """Q8_K quantization of bf16 rows x [R, K] (K a multiple of 256)."""
+    import torch
+    _need(x, "x", torch.bfloat16, 2)
+    R, K = x.shape
+    nbytes = max(moe_q8k_bytes(R, K), 16)
+    if out is None:
+        out = torch.empty((nbytes,), dtype=torch.uint8, device=x.device)
+    _need(out, "xq", torch.uint8)
+    if out.numel() < nbytes:
+        raise MoeError(3, f"xq holds {out.numel()} bytes, {nbytes} needed")
+    _check(load().moe_quantize_q8k(_ptr(x), R, K, _ptr(out), _stream(stream)))
+    return Q8KBuffer(out, R, K)
+
+
+def _need_q4k(w, name, K):
+    import torch
+    _need(w, name, torch.uint8, 4)
+    if w.shape[2] * 256 != K or w.shape[3] != Q4K_BLOCK:
+        raise MoeError(3, f"{name} must be Q4_K blocks [E, R, {K // 256}, {Q4K_BLOCK}], got "
+                          f"{tuple(w.shape)}")
+
+
+def moe_grouped_qgemm_gateup_silu(xq, w_gu, sorted_pairs, expert_offsets, K, act=None,
+                                  stream=None):
+    """xq: Q8KBuffer of x [T, H]; w_gu: Q4_K blocks uint8 [E, 2I, H/256, 144]."""
+    import torch
+    T, H = xq.R, xq.K
+    _need_q4k(w_gu, "w_gu", H)
+    E, I = w_gu.shape[0], w_gu.shape[1] // 2
+    if sorted_pairs is not None:
+        _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * K,))
+    if expert_offsets is not None:
+        _need(expert_offsets, "expert_offsets", torch.int32, shape=(E + 1,))
+    if act is None:
+        act = torch.empty((T * K, I), dtype=torch.bfloat16, device=w_gu.device)
+    _need(act, "act", torch.bfloat16, shape=(T * K, I))
+    _check(load().moe_grouped_qgemm_gateup_silu(
+        _ptr(xq.data), T, H, _ptr(w_gu), MOE_Q4_K, E, I, _ptr(sorted_pairs),
+        _ptr(expert_offsets), K, _ptr(act), _stream(stream)))
+    return act
+
+
+def moe_grouped_qgemm_down(actq, w_d, sorted_pairs, expert_offsets, pair_w, expert_out=None,
+                           stream=None):
+    """actq: Q8KBuffer of act [P, I]; w_d: Q4_K blocks uint8 [E, H, I/256, 144]."""
+    import torch
+    P, I = actq.R, actq.K
+    _need_q4k(w_d, "w_d", I)
+    E, H = w_d.shape[0], w_d.shape[1]
+    if sorted_pairs is not None:
+        _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(P,))
+    if expert_offsets is not None:
+        _need(expert_offsets, "expert_offsets", torch.int32, shape=(E + 1,))
+    if pair_w is not None:
+        _need(pair_w, "pair_w", torch.float32)
+        if pair_w.numel() != P:
+            raise MoeError(3, f"pair_w must hold {P} weights, got {pair_w.numel()}")
+    if expert_out is None:
+        expert_out = torch.empty((P, H), dtype=torch.bfloat16, device=w_d.device)
+    _need(expert_out, "expert_out", torch.bfloat16, shape=(P, H))
+    _check(load().moe_grouped_qgemm_down(
+        _ptr(actq.data), P, I, _ptr(w_d), MOE_Q4_K, E, H, _ptr(sorted_pairs),
+        _ptr(expert_offsets), _ptr(pair_w), _ptr(expert_out), _stream(stream)))
     return expert_out
 
 

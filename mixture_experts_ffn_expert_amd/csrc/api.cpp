@@ -160,6 +160,138 @@ moe_status moe_pack_weights(const uint16_t* w, int E, int R, int K, moe_pack_kin
                                          static_cast<hipStream_t>(stream)));
 }
 
+// ---------------------------------------------------------------------------
+// Keep-quant path: Q8_K activation buffers and the Q4_K grouped GEMMs.
+// ---------------------------------------------------------------------------
+namespace {
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Q8KView {
+  size_t qs, d, bs, total;  // byte offsets of the sections and the total size
+};
+
+Q8KView q8k_view(int R, int K) {
+  Q8KView v;
+  v.qs = 0;
+  v.d = align256((size_t)R * K);
+  v.bs = align256(v.d + (size_t)R * (K / 256) * 4);
+  v.total = align256(v.bs + (size_t)R * (K / 16) * 4);
+  return v;
+}
+
+bool q8k_shape_ok(int R, int K) {
+  return R >= 0 && K >= 256 && K % 256 == 0 && (long long)R * K < (1LL << 31);
+}
+
+}  // namespace
+
+size_t moe_q8k_bytes(int R, int K) {
+  if (!q8k_shape_ok(R, K) || R == 0) return 0;
+  return q8k_view(R, K).total;
+}
+
+moe_status moe_quantize_q8k(const uint16_t* x, int R, int K, void* xq, moe_stream_t stream) {
+  const char* fn = "moe_quantize_q8k";
+  clear_err();
+  if (!q8k_shape_ok(R, K))
+    return fail(MOE_E_SHAPE, "%s: K=%d must be a positive multiple of 256 and R*K below 2^31 "
+                "(R=%d)", fn, K, R);
+  if (R == 0) return MOE_OK;
+  REQUIRE_PTR(fn, x);
+  REQUIRE_PTR(fn, xq);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  const Q8KView v = q8k_view(R, K);
+  unsigned char* b = static_cast<unsigned char*>(xq);
+  return hip_status(fn, moe::launch_quantize_q8k(x, R, K, reinterpret_cast<int8_t*>(b + v.qs),
+                                                 reinterpret_cast<float*>(b + v.d),
+                                                 reinterpret_cast<int32_t*>(b + v.bs),
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+static moe_status kq_common(const char* fn, moe_qtype wt, int E, int R, int Kd) {
+  if (wt != MOE_Q4_K)
+    return fail(MOE_E_DTYPE, "%s: weight type %d unsupported (only MOE_Q4_K exists)", fn,
+                (int)wt);
+  if (E < 1 || E > kMaxE) return fail(MOE_E_SHAPE, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if (Kd < 256 || Kd % 256)
+    return fail(MOE_E_SHAPE, "%s: the reduced dimension %d must be a positive multiple of 256", fn,
+                Kd);
+  if ((long long)R * (Kd / 256) * 144 >= (1LL << 31))
+    return fail(MOE_E_SHAPE, "%s: one expert's Q4_K weights exceed 2^31 bytes", fn);
+  return MOE_OK;
+}
+
+moe_status moe_grouped_qgemm_gateup_silu(const void* xq, int T, int H, const void* w_gu,
+                                         moe_qtype wt, int E, int I, const int32_t* sorted_pairs,
+                                         const int32_t* expert_offsets, int K, uint16_t* act,
+                                         moe_stream_t stream) {
+  const char* fn = "moe_grouped_qgemm_gateup_silu";
+  clear_err();
+  if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
+  moe_status st = kq_common(fn, wt, E, 2 * I, H);
+  if (st != MOE_OK) return st;
+  if (I <= 0 || I % 8) return fail(MOE_E_SHAPE, "%s: I=%d must be a positive multiple of 8", fn, I);
+  if (K < 1 || K > E || K > kMaxK)
+    return fail(MOE_E_SHAPE, "%s: K=%d outside [1, min(E=%d, %d)]", fn, K, E, kMaxK);
+  if ((sorted_pairs == nullptr) != (expert_offsets == nullptr))
+    return fail(MOE_E_INVALID, "%s: sorted_pairs and expert_offsets must both be set or both NULL",
+                fn);
+  if (sorted_pairs == nullptr && (E != 1 || K != 1))
+    return fail(MOE_E_INVALID, "%s: identity rows (NULL sorted_pairs) need E=1 and K=1, got E=%d K=%d",
+                fn, E, K);
+  if (!q8k_shape_ok(T, H) || !fits_i32((long long)T * K * I))
+    return fail(MOE_E_SHAPE, "%s: T*H or T*K*I exceeds 2^31", fn);
+  if (T == 0) return MOE_OK;
+  REQUIRE_PTR(fn, xq);
+  REQUIRE_PTR(fn, w_gu);
+  REQUIRE_PTR(fn, act);
+  st = check_device(fn);
+  if (st != MOE_OK) return st;
+  const Q8KView v = q8k_view(T, H);
+  const unsigned char* b = static_cast<const unsigned char*>(xq);
+  return hip_status(fn, moe::launch_kq_gateup_silu(
+                            reinterpret_cast<const int8_t*>(b + v.qs),
+                            reinterpret_cast<const float*>(b + v.d),
+                            reinterpret_cast<const int32_t*>(b + v.bs), T, H,
+                            static_cast<const uint8_t*>(w_gu), E, I, sorted_pairs, expert_offsets,
+                            K, act, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_qgemm_down(const void* actq, int P, int I, const void* w_d, moe_qtype wt,
+                                  int E, int H, const int32_t* sorted_pairs,
+                                  const int32_t* expert_offsets, const float* pair_w,
+                                  uint16_t* expert_out, moe_stream_t stream) {
+  const char* fn = "moe_grouped_qgemm_down";
+  clear_err();
+  if (P < 0) return fail(MOE_E_SHAPE, "%s: P=%d is negative", fn, P);
+  moe_status st = kq_common(fn, wt, E, H, I);
+  if (st != MOE_OK) return st;
+  if (H <= 0 || H % 8) return fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);
+  if ((sorted_pairs == nullptr) != (expert_offsets == nullptr))
+    return fail(MOE_E_INVALID, "%s: sorted_pairs and expert_offsets must both be set or both NULL",
+                fn);
+  if (sorted_pairs == nullptr && E != 1)
+    return fail(MOE_E_INVALID, "%s: identity rows (NULL sorted_pairs) need E=1, got E=%d", fn, E);
+  if (!q8k_shape_ok(P, I) || !fits_i32((long long)P * H))
+    return fail(MOE_E_SHAPE, "%s: P*I or P*H exceeds 2^31", fn);
+  if (P == 0) return MOE_OK;
+  REQUIRE_PTR(fn, actq);
+  REQUIRE_PTR(fn, w_d);
+  REQUIRE_PTR(fn, expert_out);
+  st = check_device(fn);
+  if (st != MOE_OK) return st;
+  const Q8KView v = q8k_view(P, I);
+  const unsigned char* b = static_cast<const unsigned char*>(actq);
+  return hip_status(fn, moe::launch_kq_down(reinterpret_cast<const int8_t*>(b + v.qs),
+                                            reinterpret_cast<const float*>(b + v.d),
+                                            reinterpret_cast<const int32_t*>(b + v.bs), P, I,
+                                            static_cast<const uint8_t*>(w_d), E, H, sorted_pairs,
+                                            expert_offsets, pair_w, expert_out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
                              const float* bias, float* out, moe_stream_t stream) {
   const char* fn = "moe_router_logits";

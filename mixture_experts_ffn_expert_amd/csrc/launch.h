@@ -49,4 +49,15 @@ hipError_t launch_combine(const void* eo, int eo_bf16, int T, int K, int H, cons
                           float routed_scale, const void* shared, int sh_bf16,
                           const float* gate_logit, void* out, int out_bf16, hipStream_t s);
 
+// keepquant.hip
+hipError_t launch_quantize_q8k(const uint16_t* x, int R, int K, int8_t* qs, float* d,
+                               int32_t* bsums, hipStream_t s);
+hipError_t launch_kq_gateup_silu(const int8_t* xq, const float* xd, const int32_t* xs, int T, int H,
+                                 const uint8_t* w_gu, int E, int I, const int32_t* sorted,
+                                 const int32_t* offsets, int K, uint16_t* act, hipStream_t s);
+hipError_t launch_kq_down(const int8_t* aq, const float* ad, const int32_t* as, int P, int I,
+                          const uint8_t* w_d, int E, int H, const int32_t* sorted,
+                          const int32_t* offsets, const float* pair_w, uint16_t* out,
+                          hipStream_t s);
+
 }  // namespace moe

@@ -210,3 +210,17 @@ def test_pack_refusals(lib):
     assert lib.moe_pack_weights(A, 2, 40, 16, 2, A2, None) == 1 and "kind" in _err(lib)
     assert lib.moe_pack_weights(MIS, 2, 40, 16, 0, A2, None) == 1 and "aligned" in _err(lib)
     assert lib.moe_pack_weights(A, 2, 40, 16, 0, None, None) == 1 and "packed" in _err(lib)
+
+
+def test_keepquant_refusals(lib):
+    assert lib.moe_q8k_bytes(4, 300) == 0 and lib.moe_q8k_bytes(0, 256) == 0
+    assert lib.moe_q8k_bytes(4, 512) == 2048 + 256 + 512       # quants, scales, sums (aligned)
+    assert lib.moe_quantize_q8k(A, 4, 300, A2, None) == 3 and "256" in _err(lib)
+    q = lib.moe_grouped_qgemm_gateup_silu
+    assert q(A, 4, 512, A2, 2, 8, 256, A, A, 2, A, None) == 2 and "MOE_Q4_K" in _err(lib)
+    assert q(A, 4, 500, A2, 12, 8, 256, A, A, 2, A, None) == 3
+    assert q(A, 4, 512, A2, 12, 8, 256, None, A, 2, A, None) == 1 and "both" in _err(lib)
+    d = lib.moe_grouped_qgemm_down
+    assert d(A, 8, 300, A2, 12, 8, 512, A, A, None, A, None) == 3
+    assert d(A, 8, 256, A2, 12, 2, 512, None, None, None, A, None) == 1 and "E=1" in _err(lib)
+    assert q(None, 0, 512, None, 12, 8, 256, A, A, 2, None, None) == 0
