@@ -43,6 +43,21 @@ def algorithmic_work(cfg, offsets):
     P = T * K
     counts = np.diff(offsets)
     touched = int(np.count_nonzero(counts))
+    if getattr(cfg, "weights", "bf16") == "q4_k":
+        # Q4_K weights: 144 bytes per 256; Q8_K activations: 1 byte per value
+        # plus a 4-byte scale per 256 and a 4-byte sum per 16
+        q8 = lambda rows, k: rows * k + rows * (k // 256) * 4 + rows * (k // 16) * 4
+        gu = {
+            "flops": 2.0 * P * (2 * I) * H,
+            "bytes": touched * 2 * I * (H // 256) * 144 + q8(T, H) + P * I * 2 + P * 4
+                     + (E + 1) * 4,
+        }
+        dn = {
+            "flops": 2.0 * P * H * I,
+            "bytes": touched * H * (I // 256) * 144 + q8(P, I) + P * H * 2 + P * 4 + P * 4
+                     + (E + 1) * 4,
+        }
+        return gu, dn, touched
     gu = {
         "flops": 2.0 * P * (2 * I) * H,
         # weights of touched experts once + x once + act written + routing arrays
@@ -174,12 +189,17 @@ def main():
     # format change, outside the timed region)
     pack_kind = {"w_gu": "gateup", "w_d": "plain", "w_gu_s": "gateup", "w_d_s": "plain"}
     names = [n for n in ("w_r", "w_gu", "w_d", "w_gu_s", "w_d_s", "w_g") if n in d]
+    keepquant = cfg.weights == "q4_k"
     layers = []
     for _ in range(max(1, args.layers)):
         lw = {}
         for n in names:
             t = bf(d[n])
             lw[n] = moe.moe_pack_weights(t, pack_kind[n]) if n in pack_kind else t
+        if keepquant:
+            # Q4_K blocks are used as they are (keep-quant)
+            lw["w_gu"] = torch.from_numpy(d["w_gu_q4k"]).to(dev)
+            lw["w_d"] = torch.from_numpy(d["w_d_q4k"]).to(dev)
         torch.cuda.synchronize()
         layers.append(lw)
     T, H, E, K, I = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I
@@ -210,15 +230,26 @@ def main():
                 topk_w=bufs.get("w"), expert_offsets=bufs.get("offsets"),
                 sorted_pairs=bufs.get("sorted"), workspace=ws)
         bufs.update(ids=ids, w=w, offsets=off, sorted=sp)
+        if keepquant:
+            xq = moe.moe_quantize_q8k(x, bufs.get("xq_buf"))
+            bufs["xq_buf"] = xq.data
         if record:
             # the GEMM kernels record their own start and end (no packets
             # added to the queue), on the stream they run on
             evs = record
             moe.moe_time_next_gemm(evs[0], evs[1])
-        act = moe.moe_grouped_gemm_gateup_silu(x, w_gu, sp, off, K, bufs.get("act"))
+        if keepquant:
+            act = moe.moe_grouped_qgemm_gateup_silu(xq, w_gu, sp, off, K, bufs.get("act"))
+            aq = moe.moe_quantize_q8k(act, bufs.get("aq_buf"))
+            bufs["aq_buf"] = aq.data
+        else:
+            act = moe.moe_grouped_gemm_gateup_silu(x, w_gu, sp, off, K, bufs.get("act"))
         if record:
             moe.moe_time_next_gemm(evs[2], evs[3])
-        eo = moe.moe_grouped_gemm_down(act, w_d, sp, off, w, bufs.get("expert_out"))
+        if keepquant:
+            eo = moe.moe_grouped_qgemm_down(aq, w_d, sp, off, w, bufs.get("expert_out"))
+        else:
+            eo = moe.moe_grouped_gemm_down(act, w_d, sp, off, w, bufs.get("expert_out"))
         if record:
             ev.append(evs)
         bufs.update(act=act, expert_out=eo)
@@ -277,7 +308,8 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
     roof["traffic"] = measured_traffic(args.workload)
-    roof["kernel"] = "grouped gate-up GEMM + SiLU-mul"
+    roof["kernel"] = ("grouped keep-quant gate-up GEMM + SiLU-mul (Q4_K)" if keepquant
+                      else "grouped gate-up GEMM + SiLU-mul")
     roof["algorithmic"] = {"bytes_per_launch": gu["bytes"], "flops_per_launch": gu["flops"],
                            "touched_experts": touched}
     gemm_ms = gu_ms + dn_ms
@@ -295,8 +327,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1/fan_in) bf16 weights of the workload's shapes)",
+        "dtype": "q4_k weights, q8_k activations, i8 MFMA" if keepquant else "bf16",
+        "data": ("synthetic (seeded random valid Q4_K expert blocks, N(0,1/fan_in) router "
+                 "weights, of the workload's shapes)" if keepquant else
+                 "synthetic (seeded N(0,1/fan_in) bf16 weights of the workload's shapes)"),
         "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "K": K, "I": I,
                    "I_shared": cfg.I_s, "skewed_router": cfg.skew_bias, "router": cfg.router,
                    "parallelism": "single GPU"},
@@ -315,7 +349,7 @@ def main():
     if not args.no_cpu_baseline:
         # about 10-30 s of CPU work at most: all tokens of the small workloads,
         # a prefix of the large ones
-        sample = {1: 16, 2: 32, 3: 256, 4: 128, 5: 64, 6: 128}.get(args.workload, 32)
+        sample = {1: 16, 2: 32, 3: 256, 4: 128, 5: 64, 6: 128, 7: 32}.get(args.workload, 32)
         res["cpu_baseline"] = cpu_baseline(d, min(sample, T))
     print(json.dumps(res))
 

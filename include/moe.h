@@ -85,7 +85,8 @@ const char* moe_last_error(void);
 moe_status moe_init(void);
 
 /* Measurement only. Arms kernel timing for the next GEMM call
- * (moe_router_logits, moe_grouped_gemm_gateup_silu or moe_grouped_gemm_down)
+ * (moe_router_logits, moe_grouped_gemm_gateup_silu, moe_grouped_gemm_down,
+ * moe_grouped_qgemm_gateup_silu or moe_grouped_qgemm_down)
  * made by this host thread: its kernel is launched so that it records its
  * own start and end into `start` and `stop` (hipEvent_t created by the
  * caller), and hipEventElapsedTime(start, stop) then gives the kernel's

@@ -228,6 +228,7 @@ moe_status moe_grouped_qgemm_gateup_silu(const void* xq, int T, int H, const voi
                                          const int32_t* expert_offsets, int K, uint16_t* act,
                                          moe_stream_t stream) {
   const char* fn = "moe_grouped_qgemm_gateup_silu";
+  DisarmTiming disarm;
   clear_err();
   if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
   moe_status st = kq_common(fn, wt, E, 2 * I, H);
@@ -264,6 +265,7 @@ moe_status moe_grouped_qgemm_down(const void* actq, int P, int I, const void* w_
                                   const int32_t* expert_offsets, const float* pair_w,
                                   uint16_t* expert_out, moe_stream_t stream) {
   const char* fn = "moe_grouped_qgemm_down";
+  DisarmTiming disarm;
   clear_err();
   if (P < 0) return fail(MOE_E_SHAPE, "%s: P=%d is negative", fn, P);
   moe_status st = kq_common(fn, wt, E, H, I);

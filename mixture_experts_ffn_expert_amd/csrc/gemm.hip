@@ -972,6 +972,15 @@ void set_gemm_timing(hipEvent_t start, hipEvent_t stop) {
   t_stop = stop;
 }
 
+hipError_t timed_launch(const void* kernel, dim3 grid, dim3 block, void** args, hipStream_t s) {
+  if (t_start != nullptr && t_stop != nullptr) {
+    const hipEvent_t a = t_start, b = t_stop;
+    t_start = t_stop = nullptr;
+    return hipExtLaunchKernel(kernel, grid, block, args, 0, s, a, b, 0);
+  }
+  return hipLaunchKernel(kernel, grid, block, args, 0, s);
+}
+
 template <typename Kernel>
 static hipError_t run(Kernel kernel, unsigned grid, unsigned block, hipStream_t s, GemmArgs& g) {
   if (t_start != nullptr && t_stop != nullptr) {

@@ -87,9 +87,11 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const uint16_t* __res
 
 // ---------------------------------------------------------------------------
 // Grouped keep-quant GEMM, few rows per expert (decode): one workgroup = one
-// 16-row tile of one expert x 16 output columns (gate-up: the 16 gate rows
-// and the 16 matching up rows); its KS waves split the super-blocks and add
-// their partial f32 tiles in LDS in a fixed order.
+// 16-row tile of one expert x 16*NFO output columns (gate-up: each group of
+// 16 gate rows with the 16 matching up rows); its KS waves split the
+// super-blocks and add their partial f32 tiles in LDS in a fixed order. The
+// activation side of a super-block (A operands, scales, sums) is loaded once
+// per wave and used by all its weight fragments.
 // ---------------------------------------------------------------------------
 struct KqArgs {
   const int8_t* xq;        // activation quants [a_rows, kdim]
@@ -166,10 +168,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kq_rsrc(const void* base, size
 
 constexpr uint32_t kqOob = 0x80000000u;
 
-template <int EPI, int KS>
+template <int EPI, int KS, int NFO>
 __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
 #pragma clang fp contract(off)
-  constexpr int NB = (EPI == KQ_GATEUP) ? 2 : 1;  // weight fragments (gate, up)
+  // weight fragments of 16 rows: NFO column groups, each gate (and up)
+  constexpr int NB = (EPI == KQ_GATEUP) ? 2 * NFO : NFO;
   __shared__ float red[KS][NB][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
   const int nb = blockIdx.x - slot * g.nblk;
   int e, row0, rows;
   if (!kq_find_tile(g, slot, e, row0, rows)) return;  // uniform over the workgroup
-  const int col0 = nb * 16;
+  const int col0 = nb * 16 * NFO;
   const int r16 = lane & 15;   // A row / B column of this lane's MFMA operands
   const int kc = lane >> 4;    // 8-value k chunk of a 32-value sub-block
   const int nsb = g.kdim / kQK;
@@ -206,12 +209,14 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
   const __amdgpu_buffer_rsrc_t rw =
       kq_rsrc(g.W + (size_t)e * g.b_rows * row_bytes, (size_t)g.b_rows * row_bytes);
 
-  // byte offsets (super-block 0) of this lane's weight rows
+  // byte offsets (super-block 0) of this lane's weight rows: fragment f is
+  // column group f / 2 (gate-up: f even gate, f odd up) or f (down)
   uint32_t wrow[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f) {
-    const int c = col0 + r16;
-    const int wr = (EPI == KQ_GATEUP && f == 1) ? g.n_out + c : c;
+    const int fo = (EPI == KQ_GATEUP) ? (f >> 1) : f;
+    const int c = col0 + fo * 16 + r16;
+    const int wr = (EPI == KQ_GATEUP && (f & 1)) ? g.n_out + c : c;
     wrow[f] = (c < g.n_out) ? (uint32_t)(wr * row_bytes) : kqOob;
   }
   const uint32_t aq_off = (arow >= 0) ? (uint32_t)((size_t)arow * g.kdim) + kc * 8 : kqOob;
@@ -226,7 +231,14 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
   const int per = (nsb + KS - 1) / KS;
   const int sb0 = min(nsb, wave * per), sb1 = min(nsb, sb0 + per);
   for (int sb = sb0; sb < sb1; ++sb) {
-    // activation scale and sums of 32 (per sub-block) for the 4 C rows
+    // activation side, shared by every fragment: A operands of the 8
+    // sub-blocks, the scale and the sums of 32 of the 4 C rows
+    long aop[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t ao = (aq_off == kqOob) ? kqOob : aq_off + sb * kQK + j * 32;
+      aop[j] = (long)__builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rq, ao, 0, 0));
+    }
     float dx[4];
     int bs32[4][8];
 #pragma unroll
@@ -245,9 +257,15 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
     const uint32_t sboff = (uint32_t)sb * kQ4KBytes;
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
-      // header: f16 d, f16 dmin, 12 bytes of six-bit scales and mins
+      // header: f16 d, f16 dmin, 12 bytes of six-bit scales and mins; quants
       const uint32_t ho = (wrow[f] == kqOob) ? kqOob : wrow[f] + sboff;
       const i32x4v hdr = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(rw, ho, 0, 0));
+      uint2 w8[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t qo = (ho == kqOob) ? kqOob : ho + 16 + p * 32 + kc * 8;
+        w8[p] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, qo, 0, 0));
+      }
       const float dw = (float)__builtin_bit_cast(_Float16, (uint16_t)(hdr.x & 0xFFFF));
       const float dmw = (float)__builtin_bit_cast(_Float16, (uint16_t)((uint32_t)hdr.x >> 16));
       uint8_t sc12[12];
@@ -272,18 +290,14 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
       int sumi[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const uint32_t qo = (ho == kqOob) ? kqOob : ho + 16 + p * 32 + kc * 8;
-        const uint2 w8 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, qo, 0, 0));
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int j = 2 * p + half;
-          const uint32_t lo = half ? ((w8.x >> 4) & 0x0F0F0F0Fu) : (w8.x & 0x0F0F0F0Fu);
-          const uint32_t hi = half ? ((w8.y >> 4) & 0x0F0F0F0Fu) : (w8.y & 0x0F0F0F0Fu);
+          const uint32_t lo = half ? ((w8[p].x >> 4) & 0x0F0F0F0Fu) : (w8[p].x & 0x0F0F0F0Fu);
+          const uint32_t hi = half ? ((w8[p].y >> 4) & 0x0F0F0F0Fu) : (w8[p].y & 0x0F0F0F0Fu);
           const long bop = (long)(((uint64_t)hi << 32) | lo);
-          const uint32_t ao = (aq_off == kqOob) ? kqOob : aq_off + sb * kQK + j * 32;
-          const long aop = (long)__builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rq, ao, 0, 0));
           const i32x4v z = {0, 0, 0, 0};
-          const i32x4v dot = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, z, 0, 0, 0);
+          const i32x4v dot = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[j], bop, z, 0, 0, 0);
           sumi[0] += sc[j] * dot.x;
           sumi[1] += sc[j] * dot.y;
           sumi[2] += sc[j] * dot.z;
@@ -312,28 +326,33 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
   // C layout: element i of lane l is row (l/16)*4 + i, column l%16; wave w
   // finishes the elements i = w, w + KS, ...: fixed-order sum over waves
   for (int i = wave; i < 4; i += KS) {
-    float sum[NB];
-#pragma unroll
-    for (int f = 0; f < NB; ++f) {
-      float s = red[0][f][i][lane];
-#pragma unroll
-      for (int w = 1; w < KS; ++w) s = s + red[w][f][i][lane];
-      sum[f] = s;
-    }
     const int rr = kc * 4 + i;
-    const int c = col0 + r16;
-    if (rr >= rows || c >= g.n_out) continue;
+    if (rr >= rows) continue;
     const int q = row0 + rr;
-    if (EPI == KQ_GATEUP) {
-      const float gb = round_bf16(sum[0]);  // N1
-      const float ub = round_bf16(sum[NB - 1]);
-      g.out[(size_t)q * g.n_out + c] = (uint16_t)f32_to_bf16(silu_cw(gb) * ub);
-    } else {
-      const int p = (g.sorted != nullptr) ? g.sorted[q] : q;
-      if (p < 0 || p >= g.P) continue;
-      float y = sum[0];
-      if (g.pair_w != nullptr) y = y * g.pair_w[p];  // N2
-      g.out[(size_t)p * g.n_out + c] = (uint16_t)f32_to_bf16(y);
+#pragma unroll
+    for (int fo = 0; fo < NFO; ++fo) {
+      const int c = col0 + fo * 16 + r16;
+      constexpr int PER = (EPI == KQ_GATEUP) ? 2 : 1;
+      float sum[PER];
+#pragma unroll
+      for (int h = 0; h < PER; ++h) {
+        float s = red[0][fo * PER + h][i][lane];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) s = s + red[w][fo * PER + h][i][lane];
+        sum[h] = s;
+      }
+      if (c >= g.n_out) continue;
+      if (EPI == KQ_GATEUP) {
+        const float gb = round_bf16(sum[0]);  // N1
+        const float ub = round_bf16(sum[PER - 1]);
+        g.out[(size_t)q * g.n_out + c] = (uint16_t)f32_to_bf16(silu_cw(gb) * ub);
+      } else {
+        const int p = (g.sorted != nullptr) ? g.sorted[q] : q;
+        if (p < 0 || p >= g.P) continue;
+        float y = sum[0];
+        if (g.pair_w != nullptr) y = y * g.pair_w[p];  // N2
+        g.out[(size_t)p * g.n_out + c] = (uint16_t)f32_to_bf16(y);
+      }
     }
   }
 }
@@ -351,21 +370,25 @@ hipError_t launch_quantize_q8k(const uint16_t* x, int R, int K, int8_t* qs, floa
   return hipGetLastError();
 }
 
-template <int EPI>
-static hipError_t kq_launch(KqArgs g, hipStream_t s) {
-  g.nblk = (g.n_out + 15) / 16;
+template <int EPI, int KS, int NFO>
+static hipError_t kq_launch_shape(KqArgs g, hipStream_t s) {
+  g.nblk = (g.n_out + 16 * NFO - 1) / (16 * NFO);
   g.slots = kq_slots(g.P, g.E, g.offsets != nullptr);
   const unsigned grid = (unsigned)((long long)g.slots * g.nblk);
+  void* args[] = {&g};
+  return timed_launch(reinterpret_cast<const void*>(kq_stream_kernel<EPI, KS, NFO>), dim3(grid),
+                      dim3(64 * KS), args, s);
+}
+
+// k split over as many waves as there are super-blocks (at most 4); 64
+// output columns per workgroup
+template <int EPI>
+static hipError_t kq_launch(KqArgs g, hipStream_t s) {
   const int nsb = g.kdim / kQK;
-  if (nsb >= 4)
-    hipLaunchKernelGGL((kq_stream_kernel<EPI, 4>), dim3(grid), dim3(256), 0, s, g);
-  else if (nsb == 3)
-    hipLaunchKernelGGL((kq_stream_kernel<EPI, 3>), dim3(grid), dim3(192), 0, s, g);
-  else if (nsb == 2)
-    hipLaunchKernelGGL((kq_stream_kernel<EPI, 2>), dim3(grid), dim3(128), 0, s, g);
-  else
-    hipLaunchKernelGGL((kq_stream_kernel<EPI, 1>), dim3(grid), dim3(64), 0, s, g);
-  return hipGetLastError();
+  if (nsb >= 4) return kq_launch_shape<EPI, 4, 4>(g, s);
+  if (nsb == 3) return kq_launch_shape<EPI, 3, 4>(g, s);
+  if (nsb == 2) return kq_launch_shape<EPI, 2, 4>(g, s);
+  return kq_launch_shape<EPI, 1, 4>(g, s);
 }
 
 hipError_t launch_kq_gateup_silu(const int8_t* xq, const float* xd, const int32_t* xs, int T, int H,

@@ -41,6 +41,9 @@ hipError_t launch_down(const uint16_t* act, int P, int I, const uint16_t* w_d, i
 // Arms kernel timing for the next GEMM launch on this host thread (both null:
 // disarm).
 void set_gemm_timing(hipEvent_t start, hipEvent_t stop);
+// Launch through hipExtLaunchKernel with the armed events (then disarmed), or
+// plainly when none are armed.
+hipError_t timed_launch(const void* kernel, dim3 grid, dim3 block, void** args, hipStream_t s);
 hipError_t launch_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
                          const float* bias, float* out, hipStream_t s);
 

@@ -32,7 +32,7 @@ import numpy as np
 
 from .moe_oracle import F32, bf16_from_f32, f32_from_bf16, silu
 
-__all__ = ["Q4K_BLOCK", "q4k_scale_min", "q4k_unpack", "q4k_dequant", "make_q4k",
+__all__ = ["Q4K_BLOCK", "q4k_scale_min", "q4k_unpack", "q4k_dequant",
            "quantize_q8k", "q8k_dequant", "qdot_q4k_q8k", "kq_gateup_silu", "kq_down"]
 
 Q4K_BLOCK = 144   # bytes per super-block of 256 weights
@@ -80,21 +80,6 @@ def q4k_dequant(blocks: np.ndarray) -> np.ndarray:
     mnv = np.repeat(mn, 32, axis=-1).astype(np.float64)
     w = d * scv * q - dmin * mnv
     return w.reshape(w.shape[:-2] + (-1,))
-
-
-def make_q4k(rng: np.random.Generator, shape, K: int, std: float) -> np.ndarray:
-    """Valid random Q4_K blocks for a weight tensor [*shape, K] (K % 256 == 0):
-    random 6-bit scales and mins, random 4-bit quants, f16 d = dmin chosen so
-    the weights have roughly the given standard deviation."""
-    nsb = K // QK
-    full = tuple(shape) + (nsb,)
-    out = np.zeros(full + (Q4K_BLOCK,), np.uint8)
-    s = (std / 150.0) * (0.75 + 0.5 * rng.random(full))
-    out[..., 0:2] = s.astype(np.float16)[..., None].view(np.uint8)
-    out[..., 2:4] = (s * (0.75 + 0.5 * rng.random(full))).astype(np.float16)[..., None].view(np.uint8)
-    out[..., 4:16] = rng.integers(0, 256, size=full + (12,), dtype=np.uint8)
-    out[..., 16:] = rng.integers(0, 256, size=full + (128,), dtype=np.uint8)
-    return out
 
 
 def _round_half_even_f32(v: np.ndarray) -> np.ndarray:

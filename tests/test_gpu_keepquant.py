@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle as O
+import workloads as W
 from gpu_helpers import DEV, assert_bits_equal, assert_gemm_close, bits, to_dev, to_dev_bf16
 
 import mixture_experts_ffn_expert_amd as moe
@@ -78,7 +79,7 @@ def test_keepquant_gemms_stagewise(gpu_lib, T, H, E, K, I, empty):
     print(f"keep-quant T={T} H={H} E={E} K={K} I={I}", flush=True)
     g = np.random.Generator(np.random.PCG64(T + H + E + I))
     x = O.bf16_from_f32(g.standard_normal((T, H)).astype(F32))
-    wgu = O.make_q4k(g, (E, 2 * I), H, 1 / math.sqrt(H))
+    wgu = W.random_q4k_blocks(g.integers(1 << 30), (E, 2 * I), H, 1 / math.sqrt(H))
     ids, w, off, sp = _routing(T, E, K, T * 7 + E, empty)
     xq = gpu_lib.moe_quantize_q8k(to_dev_bf16(x))
     act = gpu_lib.moe_grouped_qgemm_gateup_silu(xq, torch.from_numpy(wgu).to(DEV), to_dev(sp),
@@ -87,7 +88,7 @@ def test_keepquant_gemms_stagewise(gpu_lib, T, H, E, K, I, empty):
     ref_act, _ = O.kq_gateup_silu(x, wgu, sp, off, K)
     assert_gemm_close(bits(act), ref_act, "keep-quant act")
     if I % 256 == 0:
-        wd = O.make_q4k(g, (E, H), I, 1 / math.sqrt(I))
+        wd = W.random_q4k_blocks(g.integers(1 << 30), (E, H), I, 1 / math.sqrt(I))
         aq = gpu_lib.moe_quantize_q8k(to_dev_bf16(ref_act))
         eo = gpu_lib.moe_grouped_qgemm_down(aq, torch.from_numpy(wd).to(DEV), to_dev(sp),
                                             to_dev(off), to_dev(w.reshape(-1)))
@@ -100,8 +101,8 @@ def test_keepquant_identity_rows(gpu_lib):
     T, H, I = 48, 512, 256
     g = np.random.Generator(np.random.PCG64(3))
     x = O.bf16_from_f32(g.standard_normal((T, H)).astype(F32))
-    wgu = O.make_q4k(g, (1, 2 * I), H, 1 / math.sqrt(H))
-    wd = O.make_q4k(g, (1, H), I, 1 / math.sqrt(I))
+    wgu = W.random_q4k_blocks(g.integers(1 << 30), (1, 2 * I), H, 1 / math.sqrt(H))
+    wd = W.random_q4k_blocks(g.integers(1 << 30), (1, H), I, 1 / math.sqrt(I))
     ident = np.arange(T, dtype=np.int32)
     off = np.array([0, T], np.int32)
     act = gpu_lib.moe_grouped_qgemm_gateup_silu(gpu_lib.moe_quantize_q8k(to_dev_bf16(x)),
@@ -114,3 +115,33 @@ def test_keepquant_identity_rows(gpu_lib):
     torch.cuda.synchronize()
     ref_sd, _ = O.kq_down(ref_act, wd, ident, off, None)
     assert_gemm_close(bits(sd), ref_sd, "identity down")
+
+
+def test_keepquant_decode_layer(gpu_lib):
+    """The keep-quant decode workload through the GPU chain: routing on the
+    GPU's logits bit-exact, each GEMM stage against the oracle fed the same
+    input, the combine bit-exact."""
+    from conftest import cached_inputs
+    d = cached_inputs(7)
+    cfg = d["cfg"]
+    T, H, E, K, I = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I
+    x_d = to_dev_bf16(d["x"])
+    logits = gpu_lib.moe_router_logits(x_d, to_dev_bf16(d["w_r"]))
+    ids, w, off, sp = gpu_lib.moe_route(logits, K)
+    xq = gpu_lib.moe_quantize_q8k(x_d)
+    wgu = torch.from_numpy(d["w_gu_q4k"]).to(DEV)
+    wd = torch.from_numpy(d["w_d_q4k"]).to(DEV)
+    act = gpu_lib.moe_grouped_qgemm_gateup_silu(xq, wgu, sp, off, K)
+    eo = gpu_lib.moe_grouped_qgemm_down(gpu_lib.moe_quantize_q8k(act), wd, sp, off, w.view(-1))
+    out = gpu_lib.moe_combine_gate(eo, T, K)
+    torch.cuda.synchronize()
+    r_ids, r_w, r_off, r_sp = O.route(bits(logits), K)
+    assert_bits_equal(bits(ids), r_ids, "ids")
+    assert_bits_equal(bits(w), r_w, "weights")
+    assert_bits_equal(bits(sp), r_sp, "sorted_pairs")
+    ref_act, _ = O.kq_gateup_silu(d["x"], d["w_gu_q4k"], r_sp, r_off, K)
+    assert_gemm_close(bits(act), ref_act, "act")
+    ref_eo, _ = O.kq_down(bits(act), d["w_d_q4k"], r_sp, r_off, r_w.reshape(-1))
+    assert_gemm_close(bits(eo), ref_eo, "expert_out")
+    assert_bits_equal(bits(out), O.combine_gate(bits(eo), T, K, H, None, 1.0, None, None),
+                      "combine")

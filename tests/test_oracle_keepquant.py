@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 
 import oracle as O
+import workloads as W
 
 F32 = np.float32
 
@@ -115,7 +116,7 @@ def test_planted_unsigned_max_changes_codes():
 @pytest.mark.parametrize("K", [256, 768, 2048])
 def test_qdot_equals_dequantized_product(K):
     g = np.random.Generator(np.random.PCG64(K))
-    w = O.make_q4k(g, (24,), K, 1 / math.sqrt(K))
+    w = W.random_q4k_blocks(g.integers(1 << 30), (24,), K, 1 / math.sqrt(K))
     x = g.standard_normal((5, K)).astype(F32)
     xq = O.quantize_q8k(x)
     out, mag = O.qdot_q4k_q8k(xq, w)
@@ -128,8 +129,8 @@ def test_layer_steps_against_dense_brute_force():
     g = np.random.Generator(np.random.PCG64(7))
     T, H, E, K, I = 12, 512, 4, 2, 256
     x = O.bf16_from_f32(g.standard_normal((T, H)).astype(F32))
-    wgu = O.make_q4k(g, (E, 2 * I), H, 1 / math.sqrt(H))
-    wd = O.make_q4k(g, (E, H), I, 1 / math.sqrt(I))
+    wgu = W.random_q4k_blocks(g.integers(1 << 30), (E, 2 * I), H, 1 / math.sqrt(H))
+    wd = W.random_q4k_blocks(g.integers(1 << 30), (E, H), I, 1 / math.sqrt(I))
     logits = g.standard_normal((T, E)).astype(F32)
     ids, w, off, sp = O.route(logits, K)
     act, _ = O.kq_gateup_silu(x, wgu, sp, off, K)

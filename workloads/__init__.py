@@ -11,7 +11,8 @@ Recipe (one numpy ``SeedSequence(seed)``, children spawned in a fixed order):
   child 0  x      [T,H]        ~ N(0,1)
   child 1  W_r    [E,H]        ~ N(0,1/H)
   child 2  W_gu   [E,2I,H]     ~ N(0,1/H)   one grandchild per expert
-  child 3  W_d    [E,H,I]      ~ N(0,1/I)   one grandchild per expert
+           (Q4_K workloads: random valid Q4_K blocks of that spread instead)
+  child 3  W_d    [E,H,I]      ~ N(0,1/I)   one grandchild per expert (or Q4_K)
   child 4  W_gu_s [2I_s,H]     ~ N(0,1/H)   (shared expert, if I_s > 0)
   child 5  W_d_s  [H,I_s]      ~ N(0,1/I_s)
   child 6  w_g    [H]          ~ N(0,1/H)   (shared-expert gate vector)
@@ -50,6 +51,8 @@ class MoeConfig:
     # with the largest top-2 sums stay allowed, renormalised weights and a
     # routed scale of 2.5 in the combine (the DeepSeek-V3 router shape).
     router: str = "softmax"
+    # expert weight format: "bf16", or "q4_k" (GGUF Q4_K blocks, keep-quant path)
+    weights: str = "bf16"
 
     @property
     def P(self) -> int:
@@ -59,7 +62,8 @@ class MoeConfig:
 # The five workloads: a tiny layer with a shared expert, a 128-expert top-8
 # decode layer and the same layer in prefill, a 256-expert layer with a gated
 # shared expert, and a large layer whose router bias makes routing Zipf-skewed.
-# A sixth has the 256-expert layer's shapes with the grouped sigmoid router.
+# A sixth has the 256-expert layer's shapes with the grouped sigmoid router; a
+# seventh is the decode layer with Q4_K expert weights (keep-quant path).
 CONFIGS = {
     1: MoeConfig("tiny_T16_H64_E8_K2_I32_shared32", 16, 64, 8, 2, 32, I_s=32),
     2: MoeConfig("decode_T32_H2048_E128_K8_I768", 32, 2048, 128, 8, 768),
@@ -68,6 +72,8 @@ CONFIGS = {
     5: MoeConfig("skewed_T8192_H4096_E128_K8_I1536", 8192, 4096, 128, 8, 1536, skew_bias=True),
     6: MoeConfig("grouped_T512_H2048_E256_K8_I512_shared512", 512, 2048, 256, 8, 512, I_s=512,
                  router="grouped_sigmoid"),
+    7: MoeConfig("keepquant_decode_T32_H2048_E128_K8_I768_q4k", 32, 2048, 128, 8, 768,
+                 weights="q4_k"),
 }
 
 
@@ -142,7 +148,10 @@ def make_inputs(cfg, seed: int | None = None, *, T: int | None = None,
     d = {"cfg": cfg, "seed": seed}
     d["x"] = _normal_bf16(kids[0], (cfg.T, H), 1.0)
     d["w_r"] = _normal_bf16(kids[1], (E, H), 1.0 / math.sqrt(H))
-    if experts:
+    if experts and cfg.weights == "q4_k":
+        d["w_gu_q4k"] = random_q4k_blocks(kids[2], (E, 2 * I), H, 1.0 / math.sqrt(H))
+        d["w_d_q4k"] = random_q4k_blocks(kids[3], (E, H), I, 1.0 / math.sqrt(I))
+    elif experts:
         d["w_gu"] = _per_expert_bf16(kids[2], E, (2 * I, H), 1.0 / math.sqrt(H), threads)
         d["w_d"] = _per_expert_bf16(kids[3], E, (H, I), 1.0 / math.sqrt(I), threads)
     if I_s > 0:
@@ -157,6 +166,23 @@ def make_inputs(cfg, seed: int | None = None, *, T: int | None = None,
         g = np.random.Generator(np.random.PCG64(kids[8]))
         d["selection_bias"] = g.standard_normal(E, dtype=np.float32) * np.float32(0.1)
     return d
+
+
+def random_q4k_blocks(seed, shape, K: int, std: float) -> np.ndarray:
+    """Valid random GGUF Q4_K blocks (uint8 [*shape, K/256, 144]) for weights
+    of roughly the given standard deviation: f16 d and dmin near std/150,
+    random six-bit scales and mins, random 4-bit quants. Random bytes and
+    scale values only; the format's arithmetic lives elsewhere."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    nsb = K // 256
+    full = tuple(shape) + (nsb,)
+    out = np.zeros(full + (144,), np.uint8)
+    s = (std / 150.0) * (0.75 + 0.5 * g.random(full))
+    out[..., 0:2] = s.astype(np.float16)[..., None].view(np.uint8)
+    out[..., 2:4] = (s * (0.75 + 0.5 * g.random(full))).astype(np.float16)[..., None].view(np.uint8)
+    out[..., 4:16] = g.integers(0, 256, size=full + (12,), dtype=np.uint8)
+    out[..., 16:] = g.integers(0, 256, size=full + (128,), dtype=np.uint8)
+    return out
 
 
 def random_f32(seed: int, shape, scale: float = 1.0) -> np.ndarray:
