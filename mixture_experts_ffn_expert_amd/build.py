@@ -28,6 +28,13 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
+# Per-source additions. The keep-quant kernels read every integer MFMA result
+# back right away (one scale per sub-block), so their results belong in
+# VGPRs; by default the compiler lands them in AGPRs and copies them out.
+EXTRA_FLAGS = {
+    "keepquant.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -45,7 +52,7 @@ def build(verbose: bool = False) -> str:
     def compile_one(src):
         obj = os.path.join(obj_dir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if verbose or r.returncode:
             sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)

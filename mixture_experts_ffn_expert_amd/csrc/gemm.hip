@@ -105,15 +105,15 @@ __device__ __forceinline__ bool find_tile(const GemmArgs& g, int BM, int slot, i
     const uint64_t hit = __ballot(mine);
     if (hit) {
       const int src = __ffsll((long long)hit) - 1;
-      e = __shfl(ex, src);
-      const int f = __shfl(first, src);
-      const int oo = __shfl(o0, src);
-      const int cc = __shfl(cnt, src);
+      e = __builtin_amdgcn_readlane(ex, src);
+      const int f = __builtin_amdgcn_readlane(first, src);
+      const int oo = __builtin_amdgcn_readlane(o0, src);
+      const int cc = __builtin_amdgcn_readlane(cnt, src);
       row0 = oo + (slot - f) * BM;
       rows = min(BM, cc - (slot - f) * BM);
       return true;
     }
-    before += __shfl(incl, 63);
+    before += __builtin_amdgcn_readlane(incl, 63);
   }
   return false;
 }
@@ -166,11 +166,11 @@ __device__ __forceinline__ bool find_block(const GemmArgs& g, int BM, int GM, in
     const uint64_t hit = __ballot(mine);
     if (hit) {
       const int src = __ffsll((long long)hit) - 1;
-      e = __shfl(ex, src);
-      const int f = __shfl(first, src);
-      const int oo = __shfl(o0, src);
-      const int cc = __shfl(cnt, src);
-      const int mte = __shfl(mt_e, src);
+      e = __builtin_amdgcn_readlane(ex, src);
+      const int f = __builtin_amdgcn_readlane(first, src);
+      const int oo = __builtin_amdgcn_readlane(o0, src);
+      const int cc = __builtin_amdgcn_readlane(cnt, src);
+      const int mte = __builtin_amdgcn_readlane(mt_e, src);
       const int local = L - f;
       const int full = mte / GM;
       int mg = local / (GM * g.nblk), gm = GM, rem = local - mg * GM * g.nblk;
@@ -185,7 +185,7 @@ __device__ __forceinline__ bool find_block(const GemmArgs& g, int BM, int GM, in
       rows = min(BM, cc - mt * BM);
       return true;
     }
-    before += __shfl(incl, 63);
+    before += __builtin_amdgcn_readlane(incl, 63);
   }
   return false;
 }

@@ -24,6 +24,7 @@
 namespace moe {
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kQK = 256;        // values per super-block
 constexpr int kQ4KBytes = 144;  // bytes per Q4_K super-block
@@ -144,15 +145,15 @@ __device__ __forceinline__ bool kq_find_tile(const KqArgs& g, int slot, int& e, 
     const uint64_t hit = __ballot(nt > 0 && slot >= first && slot < first + nt);
     if (hit) {
       const int src = __ffsll((long long)hit) - 1;
-      e = __shfl(ex, src);
-      const int f = __shfl(first, src);
-      const int oo = __shfl(o0, src);
-      const int cc = __shfl(cnt, src);
+      e = __builtin_amdgcn_readlane(ex, src);
+      const int f = __builtin_amdgcn_readlane(first, src);
+      const int oo = __builtin_amdgcn_readlane(o0, src);
+      const int cc = __builtin_amdgcn_readlane(cnt, src);
       row0 = oo + (slot - f) * BM;
       rows = min(BM, cc - (slot - f) * BM);
       return true;
     }
-    before += __shfl(incl, 63);
+    before += __builtin_amdgcn_readlane(incl, 63);
   }
   return false;
 }
@@ -232,60 +233,69 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
   const int sb0 = min(nsb, wave * per), sb1 = min(nsb, sb0 + per);
   for (int sb = sb0; sb < sb1; ++sb) {
     // activation side, shared by every fragment: A operands of the 8
-    // sub-blocks, the scale and the sums of 32 of the 4 C rows
+    // sub-blocks, sub-block sums, and the scales of the 4 C rows
     long aop[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t ao = (aq_off == kqOob) ? kqOob : aq_off + sb * kQK + j * 32;
       aop[j] = (long)__builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rq, ao, 0, 0));
     }
+    // A operands of the mins term: sums of the 32 quants of sub-blocks kc
+    // and kc + 4 of activation row r16
+    float bsa[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t so =
+          (arow < 0) ? kqOob : (uint32_t)(arow * (g.kdim / 16) + sb * 16 + 2 * (kc + 4 * h)) * 4;
+      const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0));
+      bsa[h] = (float)((int)s2.x + (int)s2.y);
+    }
     float dx[4];
-    int bs32[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t ro = (crow[i] >= 0) ? (uint32_t)crow[i] : kqOob;
-      dx[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                            rd, ro == kqOob ? kqOob : (ro * nsb + sb) * 4, 0, 0));
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const uint32_t so = (ro == kqOob) ? kqOob : (ro * (g.kdim / 16) + sb * 16 + h * 4) * 4;
-        const i32x4v s4 = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0));
-        bs32[i][2 * h] = s4.x + s4.y;
-        bs32[i][2 * h + 1] = s4.z + s4.w;
-      }
+      const uint32_t ro = (crow[i] >= 0) ? (uint32_t)(crow[i] * nsb + sb) * 4 : kqOob;
+      dx[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, ro, 0, 0));
     }
+    // every fragment's weight loads first (headers: f16 d, f16 dmin, 12
+    // bytes of six-bit scales and mins; then the quants), so that the
+    // whole super-block is in flight before the first MFMA
     const uint32_t sboff = (uint32_t)sb * kQ4KBytes;
+    i32x4v hdrs[NB];
+    uint2 w8s[NB][4];
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
-      // header: f16 d, f16 dmin, 12 bytes of six-bit scales and mins; quants
       const uint32_t ho = (wrow[f] == kqOob) ? kqOob : wrow[f] + sboff;
-      const i32x4v hdr = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(rw, ho, 0, 0));
-      uint2 w8[4];
+      hdrs[f] = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(rw, ho, 0, 0));
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const uint32_t qo = (ho == kqOob) ? kqOob : ho + 16 + p * 32 + kc * 8;
-        w8[p] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, qo, 0, 0));
+        w8s[f][p] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, qo, 0, 0));
       }
+    }
+#pragma unroll
+    for (int f = 0; f < NB; ++f) {
+      // one fragment at a time: keeps the MFMA results of only one
+      // fragment live
+      __builtin_amdgcn_sched_barrier(0);
+      const i32x4v hdr = hdrs[f];
+      const uint2* w8 = w8s[f];
       const float dw = (float)__builtin_bit_cast(_Float16, (uint16_t)(hdr.x & 0xFFFF));
       const float dmw = (float)__builtin_bit_cast(_Float16, (uint16_t)((uint32_t)hdr.x >> 16));
-      uint8_t sc12[12];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        sc12[b] = (uint8_t)((uint32_t)hdr.y >> (8 * b));
-        sc12[4 + b] = (uint8_t)((uint32_t)hdr.z >> (8 * b));
-        sc12[8 + b] = (uint8_t)((uint32_t)hdr.w >> (8 * b));
-      }
-      int sc[8], mn[8];
+      // scales of the 8 sub-blocks: bytes 0-3 (low 6 bits) give sc_0..3;
+      // bytes 8-11 (low nibble) with the top 2 bits of bytes 0-3 give sc_4..7
+      const uint32_t b03 = (uint32_t)hdr.y, b47 = (uint32_t)hdr.z, b811 = (uint32_t)hdr.w;
+      int sc[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sc[j] = sc12[j] & 63;
-        mn[j] = sc12[j + 4] & 63;
+        sc[j] = (b03 >> (8 * j)) & 63;
+        sc[j + 4] = ((b811 >> (8 * j)) & 0xF) | (((b03 >> (8 * j + 6)) & 3) << 4);
       }
-#pragma unroll
-      for (int j = 4; j < 8; ++j) {
-        sc[j] = (sc12[j + 4] & 0xF) | ((sc12[j - 4] >> 6) << 4);
-        mn[j] = (sc12[j + 4] >> 4) | ((sc12[j] >> 6) << 4);
-      }
+      // B operands of the mins term: m_kc and m_kc+4 of this lane's column
+      // (bytes 4-7 low 6 bits; bytes 8-11 high nibble with the top 2 bits
+      // of bytes 4-7)
+      const uint32_t sh = 8u * (uint32_t)kc;
+      const float mnb0 = (float)((b47 >> sh) & 63);
+      const float mnb1 = (float)(((b811 >> (sh + 4)) & 0xF) | (((b47 >> (sh + 6)) & 3) << 4));
       // integer sub-block dots, scaled by sc_j (this lane's column)
       int sumi[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -298,21 +308,24 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
           const long bop = (long)(((uint64_t)hi << 32) | lo);
           const i32x4v z = {0, 0, 0, 0};
           const i32x4v dot = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[j], bop, z, 0, 0, 0);
-          sumi[0] += sc[j] * dot.x;
-          sumi[1] += sc[j] * dot.y;
-          sumi[2] += sc[j] * dot.z;
-          sumi[3] += sc[j] * dot.w;
+          // |dot| <= 32 * 15 * 127 and sc_j <= 63: 24-bit products suffice
+          sumi[0] += __mul24(sc[j], dot.x);
+          sumi[1] += __mul24(sc[j], dot.y);
+          sumi[2] += __mul24(sc[j], dot.z);
+          sumi[3] += __mul24(sc[j], dot.w);
         }
       }
+      // mins term sum_j m_j bsum_j of the 4 C rows: integers below 2^21,
+      // exact in f32
+      const f32x4v zf = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4v summ = __builtin_amdgcn_mfma_f32_16x16x4f32(bsa[0], mnb0, zf, 0, 0, 0);
+      summ = __builtin_amdgcn_mfma_f32_16x16x4f32(bsa[1], mnb1, summ, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int summ = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) summ += mn[j] * bs32[i][j];
         const float dall = dw * dx[i];
         const float dmn = dmw * dx[i];
         const float t1 = dall * (float)sumi[i];
-        const float t2 = dmn * (float)summ;
+        const float t2 = dmn * summ[i];
         acc[f][i] = acc[f][i] + (t1 - t2);
       }
     }
