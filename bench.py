@@ -198,8 +198,8 @@ def main():
             lw[n] = moe.moe_pack_weights(t, pack_kind[n]) if n in pack_kind else t
         if keepquant:
             # Q4_K blocks are used as they are (keep-quant)
-            lw["w_gu"] = torch.from_numpy(d["w_gu_q4k"]).to(dev)
-            lw["w_d"] = torch.from_numpy(d["w_d_q4k"]).to(dev)
+            lw["w_gu"] = torch.from_numpy(d["w_gu_kq"]).to(dev)
+            lw["w_d"] = torch.from_numpy(d["w_d_kq"]).to(dev)
         torch.cuda.synchronize()
         layers.append(lw)
     T, H, E, K, I = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I

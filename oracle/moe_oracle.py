@@ -504,11 +504,13 @@ def moe_layer(inp: dict, logits=None, keep: bool = False) -> dict:
         routed_scale = 2.5
     else:
         ids, w, offsets, sorted_pairs = route(logits, K)
-    if getattr(cfg, "weights", "bf16") == "q4_k":
-        # keep-quant experts (Q4_K weights, Q8_K activations; see keepquant.py)
+    wtype = getattr(cfg, "weights", "bf16")
+    if wtype != "bf16":
+        # keep-quant experts (GGUF weight blocks, quantized activations; see
+        # keepquant.py)
         from .keepquant import kq_down, kq_gateup_silu
-        act, _ = kq_gateup_silu(x, inp["w_gu_q4k"], sorted_pairs, offsets, K)
-        eo, _ = kq_down(act, inp["w_d_q4k"], sorted_pairs, offsets, w.reshape(-1))
+        act, _ = kq_gateup_silu(x, inp["w_gu_kq"], sorted_pairs, offsets, K, wtype)
+        eo, _ = kq_down(act, inp["w_d_kq"], sorted_pairs, offsets, w.reshape(-1), wtype)
     else:
         act = gateup_silu(x, inp["w_gu"], sorted_pairs, offsets, K)
         eo = down_proj(act, inp["w_d"], sorted_pairs, offsets, w)

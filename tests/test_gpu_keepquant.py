@@ -129,8 +129,8 @@ def test_keepquant_decode_layer(gpu_lib):
     logits = gpu_lib.moe_router_logits(x_d, to_dev_bf16(d["w_r"]))
     ids, w, off, sp = gpu_lib.moe_route(logits, K)
     xq = gpu_lib.moe_quantize_q8k(x_d)
-    wgu = torch.from_numpy(d["w_gu_q4k"]).to(DEV)
-    wd = torch.from_numpy(d["w_d_q4k"]).to(DEV)
+    wgu = torch.from_numpy(d["w_gu_kq"]).to(DEV)
+    wd = torch.from_numpy(d["w_d_kq"]).to(DEV)
     act = gpu_lib.moe_grouped_qgemm_gateup_silu(xq, wgu, sp, off, K)
     eo = gpu_lib.moe_grouped_qgemm_down(gpu_lib.moe_quantize_q8k(act), wd, sp, off, w.view(-1))
     out = gpu_lib.moe_combine_gate(eo, T, K)
@@ -139,9 +139,9 @@ def test_keepquant_decode_layer(gpu_lib):
     assert_bits_equal(bits(ids), r_ids, "ids")
     assert_bits_equal(bits(w), r_w, "weights")
     assert_bits_equal(bits(sp), r_sp, "sorted_pairs")
-    ref_act, _ = O.kq_gateup_silu(d["x"], d["w_gu_q4k"], r_sp, r_off, K)
+    ref_act, _ = O.kq_gateup_silu(d["x"], d["w_gu_kq"], r_sp, r_off, K)
     assert_gemm_close(bits(act), ref_act, "act")
-    ref_eo, _ = O.kq_down(bits(act), d["w_d_q4k"], r_sp, r_off, r_w.reshape(-1))
+    ref_eo, _ = O.kq_down(bits(act), d["w_d_kq"], r_sp, r_off, r_w.reshape(-1))
     assert_gemm_close(bits(eo), ref_eo, "expert_out")
     assert_bits_equal(bits(out), O.combine_gate(bits(eo), T, K, H, None, 1.0, None, None),
                       "combine")

@@ -51,7 +51,8 @@ class MoeConfig:
     # with the largest top-2 sums stay allowed, renormalised weights and a
     # routed scale of 2.5 in the combine (the DeepSeek-V3 router shape).
     router: str = "softmax"
-    # expert weight format: "bf16", or "q4_k" (GGUF Q4_K blocks, keep-quant path)
+    # expert weight format: "bf16", or a GGUF block format of the keep-quant
+    # path ("q4_k", "q5_k", "q6_k", "q8_0")
     weights: str = "bf16"
 
     @property
@@ -62,8 +63,9 @@ class MoeConfig:
 # The five workloads: a tiny layer with a shared expert, a 128-expert top-8
 # decode layer and the same layer in prefill, a 256-expert layer with a gated
 # shared expert, and a large layer whose router bias makes routing Zipf-skewed.
-# A sixth has the 256-expert layer's shapes with the grouped sigmoid router; a
-# seventh is the decode layer with Q4_K expert weights (keep-quant path).
+# A sixth has the 256-expert layer's shapes with the grouped sigmoid router;
+# the seventh to tenth are the decode layer with Q4_K, Q5_K, Q6_K and Q8_0
+# expert weights (keep-quant path).
 CONFIGS = {
     1: MoeConfig("tiny_T16_H64_E8_K2_I32_shared32", 16, 64, 8, 2, 32, I_s=32),
     2: MoeConfig("decode_T32_H2048_E128_K8_I768", 32, 2048, 128, 8, 768),
@@ -74,6 +76,12 @@ CONFIGS = {
                  router="grouped_sigmoid"),
     7: MoeConfig("keepquant_decode_T32_H2048_E128_K8_I768_q4k", 32, 2048, 128, 8, 768,
                  weights="q4_k"),
+    8: MoeConfig("keepquant_decode_T32_H2048_E128_K8_I768_q5k", 32, 2048, 128, 8, 768,
+                 weights="q5_k"),
+    9: MoeConfig("keepquant_decode_T32_H2048_E128_K8_I768_q6k", 32, 2048, 128, 8, 768,
+                 weights="q6_k"),
+    10: MoeConfig("keepquant_decode_T32_H2048_E128_K8_I768_q8_0", 32, 2048, 128, 8, 768,
+                  weights="q8_0"),
 }
 
 
@@ -148,9 +156,9 @@ def make_inputs(cfg, seed: int | None = None, *, T: int | None = None,
     d = {"cfg": cfg, "seed": seed}
     d["x"] = _normal_bf16(kids[0], (cfg.T, H), 1.0)
     d["w_r"] = _normal_bf16(kids[1], (E, H), 1.0 / math.sqrt(H))
-    if experts and cfg.weights == "q4_k":
-        d["w_gu_q4k"] = random_q4k_blocks(kids[2], (E, 2 * I), H, 1.0 / math.sqrt(H))
-        d["w_d_q4k"] = random_q4k_blocks(kids[3], (E, H), I, 1.0 / math.sqrt(I))
+    if experts and cfg.weights != "bf16":
+        d["w_gu_kq"] = random_kq_blocks(cfg.weights, kids[2], (E, 2 * I), H, 1.0 / math.sqrt(H))
+        d["w_d_kq"] = random_kq_blocks(cfg.weights, kids[3], (E, H), I, 1.0 / math.sqrt(I))
     elif experts:
         d["w_gu"] = _per_expert_bf16(kids[2], E, (2 * I, H), 1.0 / math.sqrt(H), threads)
         d["w_d"] = _per_expert_bf16(kids[3], E, (H, I), 1.0 / math.sqrt(I), threads)
@@ -168,21 +176,47 @@ def make_inputs(cfg, seed: int | None = None, *, T: int | None = None,
     return d
 
 
-def random_q4k_blocks(seed, shape, K: int, std: float) -> np.ndarray:
-    """Valid random GGUF Q4_K blocks (uint8 [*shape, K/256, 144]) for weights
-    of roughly the given standard deviation: f16 d and dmin near std/150,
-    random six-bit scales and mins, random 4-bit quants. Random bytes and
-    scale values only; the format's arithmetic lives elsewhere."""
+# bytes and values per block of the GGUF weight formats
+KQ_FORMATS = {"q4_k": (144, 256), "q5_k": (176, 256), "q6_k": (210, 256), "q8_0": (34, 32)}
+
+
+def random_kq_blocks(wtype: str, seed, shape, K: int, std: float) -> np.ndarray:
+    """Valid random GGUF blocks of format wtype (uint8 [*shape, nb, bytes])
+    for weights of roughly the given standard deviation: f16 scale fields
+    drawn near std divided by the format's typical code magnitude, random
+    scale bytes and random quant bytes. Random bytes and scale values only;
+    the format's arithmetic lives elsewhere."""
+    nbytes, nval = KQ_FORMATS[wtype]
     g = np.random.Generator(np.random.PCG64(seed))
-    nsb = K // 256
-    full = tuple(shape) + (nsb,)
-    out = np.zeros(full + (144,), np.uint8)
-    s = (std / 150.0) * (0.75 + 0.5 * g.random(full))
-    out[..., 0:2] = s.astype(np.float16)[..., None].view(np.uint8)
-    out[..., 2:4] = (s * (0.75 + 0.5 * g.random(full))).astype(np.float16)[..., None].view(np.uint8)
-    out[..., 4:16] = g.integers(0, 256, size=full + (12,), dtype=np.uint8)
-    out[..., 16:] = g.integers(0, 256, size=full + (128,), dtype=np.uint8)
+    full = tuple(shape) + (K // nval,)
+    out = np.zeros(full + (nbytes,), np.uint8)
+
+    def f16(v):
+        return v.astype(np.float16)[..., None].view(np.uint8)
+
+    def jitter():
+        return 0.75 + 0.5 * g.random(full)
+
+    def rnd(n):
+        return g.integers(0, 256, size=full + (n,), dtype=np.uint8)
+
+    if wtype in ("q4_k", "q5_k"):
+        s = (std / (150.0 if wtype == "q4_k" else 300.0)) * jitter()
+        out[..., 0:2] = f16(s)
+        out[..., 2:4] = f16(s * jitter())
+        out[..., 4:] = rnd(nbytes - 4)          # scales/mins, (qh,) quants
+    elif wtype == "q6_k":
+        out[..., 0:208] = rnd(208)              # ql, qh, int8 scales
+        out[..., 208:210] = f16((std / 1400.0) * jitter())
+    else:
+        out[..., 0:2] = f16((std / 73.0) * jitter())
+        out[..., 2:34] = rnd(32)
     return out
+
+
+def random_q4k_blocks(seed, shape, K: int, std: float) -> np.ndarray:
+    """Valid random GGUF Q4_K blocks (uint8 [*shape, K/256, 144])."""
+    return random_kq_blocks("q4_k", seed, shape, K, std)
 
 
 def random_f32(seed: int, shape, scale: float = 1.0) -> np.ndarray:
