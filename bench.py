@@ -17,9 +17,10 @@ distinct weights. `hipgraph` times the same steps captured once into a HIP
 graph and replayed.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
-       (--workload picks one of the six workloads, default 2: the 32-token
+       (--workload picks one of the ten workloads, default 2: the 32-token
        decode layer with 128 experts, top-8; 6 is the 256-expert layer with
-       the grouped sigmoid router).
+       the grouped sigmoid router; 7-10 are the decode layer with Q4_K,
+       Q5_K, Q6_K and Q8_0 expert weights on the keep-quant path).
 """
 import argparse
 import dataclasses
@@ -35,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+MFMA_I8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
 
 
 def algorithmic_work(cfg, offsets):
@@ -43,18 +45,25 @@ def algorithmic_work(cfg, offsets):
     P = T * K
     counts = np.diff(offsets)
     touched = int(np.count_nonzero(counts))
-    if getattr(cfg, "weights", "bf16") == "q4_k":
-        # Q4_K weights: 144 bytes per 256; Q8_K activations: 1 byte per value
-        # plus a 4-byte scale per 256 and a 4-byte sum per 16
-        q8 = lambda rows, k: rows * k + rows * (k // 256) * 4 + rows * (k // 16) * 4
+    wtype = getattr(cfg, "weights", "bf16")
+    if wtype != "bf16":
+        # GGUF weight blocks (bytes per block of `vals` weights); activations
+        # quantized to 1 byte per value plus, per 256 values, a 4-byte scale
+        # and sixteen 4-byte sums (Q8_K), or per 32 a 2-byte scale (Q8_0)
+        blk, vals = {"q4_k": (144, 256), "q5_k": (176, 256), "q6_k": (210, 256),
+                     "q8_0": (34, 32)}[wtype]
+        if wtype == "q8_0":
+            q8 = lambda rows, k: rows * k + rows * (k // 32) * 2
+        else:
+            q8 = lambda rows, k: rows * k + rows * (k // 256) * 4 + rows * (k // 16) * 4
         gu = {
             "flops": 2.0 * P * (2 * I) * H,
-            "bytes": touched * 2 * I * (H // 256) * 144 + q8(T, H) + P * I * 2 + P * 4
+            "bytes": touched * 2 * I * (H // vals) * blk + q8(T, H) + P * I * 2 + P * 4
                      + (E + 1) * 4,
         }
         dn = {
             "flops": 2.0 * P * H * I,
-            "bytes": touched * H * (I // 256) * 144 + q8(P, I) + P * H * 2 + P * 4 + P * 4
+            "bytes": touched * H * (I // vals) * blk + q8(P, I) + P * H * 2 + P * 4 + P * 4
                      + (E + 1) * 4,
         }
         return gu, dn, touched
@@ -189,7 +198,8 @@ def main():
     # format change, outside the timed region)
     pack_kind = {"w_gu": "gateup", "w_d": "plain", "w_gu_s": "gateup", "w_d_s": "plain"}
     names = [n for n in ("w_r", "w_gu", "w_d", "w_gu_s", "w_d_s", "w_g") if n in d]
-    keepquant = cfg.weights == "q4_k"
+    wtype = cfg.weights
+    keepquant = wtype != "bf16"
     layers = []
     for _ in range(max(1, args.layers)):
         lw = {}
@@ -197,7 +207,7 @@ def main():
             t = bf(d[n])
             lw[n] = moe.moe_pack_weights(t, pack_kind[n]) if n in pack_kind else t
         if keepquant:
-            # Q4_K blocks are used as they are (keep-quant)
+            # GGUF blocks are used as they are (keep-quant)
             lw["w_gu"] = torch.from_numpy(d["w_gu_kq"]).to(dev)
             lw["w_d"] = torch.from_numpy(d["w_d_kq"]).to(dev)
         torch.cuda.synchronize()
@@ -231,7 +241,7 @@ def main():
                 sorted_pairs=bufs.get("sorted"), workspace=ws)
         bufs.update(ids=ids, w=w, offsets=off, sorted=sp)
         if keepquant:
-            xq = moe.moe_quantize_q8k(x, bufs.get("xq_buf"))
+            xq = moe.moe_quantize_act(wtype, x, bufs.get("xq_buf"))
             bufs["xq_buf"] = xq.data
         if record:
             # the GEMM kernels record their own start and end (no packets
@@ -239,15 +249,17 @@ def main():
             evs = record
             moe.moe_time_next_gemm(evs[0], evs[1])
         if keepquant:
-            act = moe.moe_grouped_qgemm_gateup_silu(xq, w_gu, sp, off, K, bufs.get("act"))
-            aq = moe.moe_quantize_q8k(act, bufs.get("aq_buf"))
+            act = moe.moe_grouped_qgemm_gateup_silu(xq, w_gu, sp, off, K, bufs.get("act"),
+                                                    wtype=wtype)
+            aq = moe.moe_quantize_act(wtype, act, bufs.get("aq_buf"))
             bufs["aq_buf"] = aq.data
         else:
             act = moe.moe_grouped_gemm_gateup_silu(x, w_gu, sp, off, K, bufs.get("act"))
         if record:
             moe.moe_time_next_gemm(evs[2], evs[3])
         if keepquant:
-            eo = moe.moe_grouped_qgemm_down(aq, w_d, sp, off, w, bufs.get("expert_out"))
+            eo = moe.moe_grouped_qgemm_down(aq, w_d, sp, off, w, bufs.get("expert_out"),
+                                            wtype=wtype)
         else:
             eo = moe.moe_grouped_gemm_down(act, w_d, sp, off, w, bufs.get("expert_out"))
         if record:
@@ -298,17 +310,20 @@ def main():
     dn_ms = float(np.mean([c.elapsed_time(d_) for _, _, c, d_ in ev]))
     offsets = bufs["offsets"].cpu().numpy()
     gu, dn, touched = algorithmic_work(cfg, offsets)
-    hbm_bound = (gu["flops"] / gu["bytes"]) < (MFMA_BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
+    # the keep-quant GEMMs run int8 MFMAs (5.0 POP/s dense)
+    mfma_peak = MFMA_I8_PEAK_TOPS if keepquant else MFMA_BF16_PEAK_TFLOPS
+    hbm_bound = (gu["flops"] / gu["bytes"]) < (mfma_peak * 1e12) / (HBM_PEAK_GBS * 1e9)
     if hbm_bound:
         achieved = gu["bytes"] / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
     else:
         achieved = gu["flops"] / (gu_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        roof = {"bound": "mfma", "achieved": achieved, "peak": mfma_peak,
+                "unit": "TOP/s" if keepquant else "TFLOP/s", "frac": achieved / mfma_peak,
+                "traffic": None}
     roof["traffic"] = measured_traffic(args.workload)
-    roof["kernel"] = ("grouped keep-quant gate-up GEMM + SiLU-mul (Q4_K)" if keepquant
+    roof["kernel"] = (f"grouped keep-quant gate-up GEMM + SiLU-mul ({wtype.upper()})" if keepquant
                       else "grouped gate-up GEMM + SiLU-mul")
     roof["algorithmic"] = {"bytes_per_launch": gu["bytes"], "flops_per_launch": gu["flops"],
                            "touched_experts": touched}
@@ -327,8 +342,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_k weights, q8_k activations, i8 MFMA" if keepquant else "bf16",
-        "data": ("synthetic (seeded random valid Q4_K expert blocks, N(0,1/fan_in) router "
+        "dtype": (f"{wtype} weights, {'q8_0' if wtype == 'q8_0' else 'q8_k'} activations, "
+                  "i8 MFMA") if keepquant else "bf16",
+        "data": (f"synthetic (seeded random valid {wtype.upper()} expert blocks, N(0,1/fan_in) router "
                  "weights, of the workload's shapes)" if keepquant else
                  "synthetic (seeded N(0,1/fan_in) bf16 weights of the workload's shapes)"),
         "config": {"workload": cfg.name, "T": T, "H": H, "E": E, "K": K, "I": I,
@@ -349,7 +365,7 @@ def main():
     if not args.no_cpu_baseline:
         # about 10-30 s of CPU work at most: all tokens of the small workloads,
         # a prefix of the large ones
-        sample = {1: 16, 2: 32, 3: 256, 4: 128, 5: 64, 6: 128, 7: 32}.get(args.workload, 32)
+        sample = {1: 16, 2: 32, 3: 256, 4: 128, 5: 64, 6: 128}.get(args.workload, 32)
         res["cpu_baseline"] = cpu_baseline(d, min(sample, T))
     print(json.dumps(res))
 

@@ -267,17 +267,29 @@ moe_status moe_combine_gate(const void* expert_out, moe_dtype eo_dt, int T, int 
 
 /*
  * Keep-quant grouped expert GEMMs ([PR 523] What changed: expert weights stay
- * in their GGUF block format, activations are quantized on the fly, dot
- * products run per super-block with an integer core). Weight type: GGUF Q4_K
- * (type number 12): per 256 weights, 144 bytes = f16 d, f16 dmin, 12 bytes of
- * six-bit sub-block scales and mins, 128 bytes of 4-bit quants; a weight
- * matrix [R, K] is R rows of K/256 such blocks, experts one after another.
- * Activations: Q8_K (per 256 values: scale d, 256 int8 quants, sums of 16).
- * Per super-block the dot product of a weight row and an activation row is
- *   d_w d_x sum_j sc_j (sum_{l in j} q4_l q8_l) - dmin_w d_x sum_j m_j bsum_j
- * (integer inside, one f32 step per super-block, f32 sum over super-blocks).
+ * in their GGUF block formats Q8_0 / Q4_K / Q5_K / Q6_K, activations are
+ * quantized on the fly by the Q8_0 and Q8_K quantizers, dot products run per
+ * block with an integer core). Weight types, by GGUF type number:
+ *   MOE_Q8_0: per 32 weights, 34 bytes = f16 d, 32 int8 quants (w = d q)
+ *   MOE_Q4_K: per 256, 144 bytes = f16 d, f16 dmin, 12 bytes of six-bit
+ *             sub-block scales and mins, 128 bytes of 4-bit quants
+ *   MOE_Q5_K: per 256, 176 bytes = as Q4_K with 32 bytes of fifth bits
+ *             between the scales and the 4-bit quants
+ *   MOE_Q6_K: per 256, 210 bytes = 128 bytes of low nibbles, 64 bytes of
+ *             2-bit high parts, 16 int8 scales of 16-value sub-blocks, f16 d
+ * A weight matrix [R, K] is R rows of K/(values per block) blocks, experts
+ * one after another; the base pointer is 16-byte aligned. K-quant weights
+ * pair with Q8_K activations, Q8_0 weights with Q8_0 activations. Per
+ * (super-)block the dot product of a weight row and an activation row is
+ *   Q4_K, Q5_K: d_w d_x sum_j sc_j (sum_{l in j} q_l q8_l) - dmin_w d_x sum_j m_j bsum_j
+ *   Q6_K:       d_w d_x sum_j sc_j (sum_{l in j} q6_l q8_l)
+ *   Q8_0:       d_w d_x sum_l q_l q8_l
+ * (integer inside, one f32 step per super-block or block, f32 sum over the
+ * row). The reduced dimension (H for gate-up, I for down) must be a positive
+ * multiple of 256 for every weight type, and one expert's blocks must stay
+ * below 2^31 bytes.
  */
-typedef enum { MOE_Q4_K = 12 } moe_qtype;
+typedef enum { MOE_Q8_0 = 8, MOE_Q4_K = 12, MOE_Q5_K = 13, MOE_Q6_K = 14 } moe_qtype;
 
 /* Bytes of the Q8_K buffer of R rows of K values (K a positive multiple of
  * 256; 0 otherwise or for R = 0). Layout, each section 256-byte aligned:
@@ -292,23 +304,37 @@ size_t moe_q8k_bytes(int R, int K);
  * d = 0, q = 0. Activations must be finite. */
 moe_status moe_quantize_q8k(const uint16_t* x, int R, int K, void* xq, moe_stream_t stream);
 
+/* Bytes of the Q8_0 buffer of R rows of K values (K a positive multiple of
+ * 32; 0 otherwise or for R = 0). Layout, each section 256-byte aligned: int8
+ * quants [R, K], then f16 scales [R, K/32]. */
+size_t moe_q8_0_bytes(int R, int K);
+
+/* Q8_0 quantization of bf16 rows x [R, K] (16-byte aligned) into xq
+ * (moe_q8_0_bytes(R, K) bytes, 16-byte aligned), per 32 values: amax = max
+ * |x|, d = amax / 127, id = 1 / d (0 when d = 0), q = round-half-away-from-
+ * zero(x * id) (f32 arithmetic), d stored as f16 (round to nearest even).
+ * Activations must be finite. */
+moe_status moe_quantize_q8_0(const uint16_t* x, int R, int K, void* xq, moe_stream_t stream);
+
 /* Keep-quant grouped gate-up with SiLU-mul ([PR 523]; [Issue 3094] N1):
- *   g, u = keep-quant dots of the Q8_K row of token t = sorted_pairs[q] / K
- *          with gate row c and up row I + c of expert e (Q4_K w_gu [E, 2I, H])
+ *   g, u = keep-quant dots of the quantized row of token t = sorted_pairs[q]
+ *          / K with gate row c and up row I + c of expert e (w_gu [E, 2I, H]
+ *          in format wt)
  *   act[q, c] = bf16(silu(bf16(g)) * bf16(u))
- * xq: moe_quantize_q8k of x [T, H]; H a multiple of 256; routing arguments,
- * act and errors as moe_grouped_gemm_gateup_silu; wt must be MOE_Q4_K
- * (MOE_E_DTYPE otherwise). */
+ * xq: moe_quantize_q8k of x [T, H] for the K-quants, moe_quantize_q8_0 for
+ * MOE_Q8_0; routing arguments, act and errors as
+ * moe_grouped_gemm_gateup_silu (NULL routing = one dense expert, E = K = 1);
+ * an unknown wt gives MOE_E_DTYPE. */
 moe_status moe_grouped_qgemm_gateup_silu(const void* xq, int T, int H, const void* w_gu,
                                          moe_qtype wt, int E, int I, const int32_t* sorted_pairs,
                                          const int32_t* expert_offsets, int K, uint16_t* act,
                                          moe_stream_t stream);
 
 /* Keep-quant grouped down projection ([PR 523]; [Issue 3094] N2, N3):
- *   y = keep-quant dot of the Q8_K row q of act with row h of expert e's
- *       Q4_K w_d [E, H, I];  expert_out[p, h] = bf16(y * pair_w[p]), p =
- *       sorted_pairs[q]
- * actq: moe_quantize_q8k of act [P, I]; I a multiple of 256; the rest as
+ *   y = keep-quant dot of the quantized row q of act with row h of expert
+ *       e's w_d [E, H, I] (format wt);  expert_out[p, h] = bf16(y *
+ *       pair_w[p]), p = sorted_pairs[q]
+ * actq: the quantizer output paired with wt, of act [P, I]; the rest as
  * moe_grouped_gemm_down. */
 moe_status moe_grouped_qgemm_down(const void* actq, int P, int I, const void* w_d, moe_qtype wt,
                                   int E, int H, const int32_t* sorted_pairs,

@@ -25,8 +25,10 @@ import os
 
 __all__ = [
     "MoeError", "load", "lib_path", "moe_init", "PackedWeights", "moe_pack_weights",
-    "moe_packed_weight_bytes", "Q8KBuffer", "moe_q8k_bytes", "moe_quantize_q8k",
-    "moe_grouped_qgemm_gateup_silu", "moe_grouped_qgemm_down", "MOE_Q4_K", "moe_router_logits", "moe_route",
+    "moe_packed_weight_bytes", "Q8KBuffer", "QBuffer", "moe_q8k_bytes", "moe_quantize_q8k",
+    "moe_q8_0_bytes", "moe_quantize_q8_0", "moe_quantize_act",
+    "moe_grouped_qgemm_gateup_silu", "moe_grouped_qgemm_down", "MOE_Q4_K", "MOE_Q5_K",
+    "MOE_Q6_K", "MOE_Q8_0", "MOE_QTYPE", "KQ_BLOCK", "moe_router_logits", "moe_route",
     "moe_route_workspace_bytes", "moe_route_scored", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
     "moe_combine_gate", "moe_layer", "moe_time_next_gemm", "MOE_F32", "MOE_BF16", "MOE_F16", "SYMBOLS",
 ]
@@ -48,6 +50,8 @@ SYMBOLS = {
     "moe_packed_weight_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "moe_q8k_bytes": (ctypes.c_size_t, [_i, _i]),
     "moe_quantize_q8k": (_st, [_p, _i, _i, _p, _p]),
+    "moe_q8_0_bytes": (ctypes.c_size_t, [_i, _i]),
+    "moe_quantize_q8_0": (_st, [_p, _i, _i, _p, _p]),
     "moe_grouped_qgemm_gateup_silu": (_st, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _i, _p, _p]),
     "moe_grouped_qgemm_down": (_st, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _p, _p, _p]),
     "moe_pack_weights": (_st, [_p, _i, _i, _i, _i, _p, _p]),
@@ -342,51 +346,89 @@ def moe_grouped_gemm_down(act, w_d, sorted_pairs, expert_offsets, pair_w, expert
     return expert_out
 
 
-MOE_Q4_K = 12
+MOE_Q8_0, MOE_Q4_K, MOE_Q5_K, MOE_Q6_K = 8, 12, 13, 14
+MOE_QTYPE = {"q8_0": MOE_Q8_0, "q4_k": MOE_Q4_K, "q5_k": MOE_Q5_K, "q6_k": MOE_Q6_K}
+# (bytes, values) per block of each weight format
+KQ_BLOCK = {"q8_0": (34, 32), "q4_k": (144, 256), "q5_k": (176, 256), "q6_k": (210, 256)}
 Q4K_BLOCK = 144
 
 
-class Q8KBuffer:
-    """Q8_K-quantized activations (``moe_quantize_q8k``): ``data`` (uint8,
-    moe_q8k_bytes(R, K) bytes) for R rows of K values."""
+class QBuffer:
+    """Quantized activations: ``data`` (uint8) holding R rows of K values in
+    the layout of ``kind`` ("q8_k": moe_quantize_q8k, "q8_0":
+    moe_quantize_q8_0)."""
 
-    def __init__(self, data, R, K):
-        self.data, self.R, self.K = data, R, K
+    def __init__(self, data, R, K, kind="q8_k"):
+        self.data, self.R, self.K, self.kind = data, R, K, kind
+
+
+Q8KBuffer = QBuffer
 
 
 def moe_q8k_bytes(R, K):
     return int(load().moe_q8k_bytes(R, K))
 
 
-def moe_quantize_q8k(x, out=None, stream=None):
-    """Q8_K quantization of bf16 rows x [R, K] (K a multiple of 256)."""
+def moe_q8_0_bytes(R, K):
+    return int(load().moe_q8_0_bytes(R, K))
+
+
+def _quantize(fn_name, kind, nbytes_fn, x, out, stream):
     import torch
     _need(x, "x", torch.bfloat16, 2)
     R, K = x.shape
-    nbytes = max(moe_q8k_bytes(R, K), 16)
+    nbytes = max(nbytes_fn(R, K), 16)
     if out is None:
         out = torch.empty((nbytes,), dtype=torch.uint8, device=x.device)
     _need(out, "xq", torch.uint8)
     if out.numel() < nbytes:
         raise MoeError(3, f"xq holds {out.numel()} bytes, {nbytes} needed")
-    _check(load().moe_quantize_q8k(_ptr(x), R, K, _ptr(out), _stream(stream)))
-    return Q8KBuffer(out, R, K)
+    _check(getattr(load(), fn_name)(_ptr(x), R, K, _ptr(out), _stream(stream)))
+    return QBuffer(out, R, K, kind)
 
 
-def _need_q4k(w, name, K):
+def moe_quantize_q8k(x, out=None, stream=None):
+    """Q8_K quantization of bf16 rows x [R, K] (K a multiple of 256)."""
+    return _quantize("moe_quantize_q8k", "q8_k", moe_q8k_bytes, x, out, stream)
+
+
+def moe_quantize_q8_0(x, out=None, stream=None):
+    """Q8_0 quantization of bf16 rows x [R, K] (K a multiple of 32)."""
+    return _quantize("moe_quantize_q8_0", "q8_0", moe_q8_0_bytes, x, out, stream)
+
+
+def moe_quantize_act(wtype, x, out=None, stream=None):
+    """The activation quantizer paired with weight format wtype."""
+    if wtype == "q8_0":
+        return moe_quantize_q8_0(x, out, stream)
+    return moe_quantize_q8k(x, out, stream)
+
+
+def _need_kq(w, name, K, wtype):
     import torch
+    if wtype not in KQ_BLOCK:
+        raise MoeError(2, f"{name}: weight format {wtype!r} unsupported ({', '.join(KQ_BLOCK)})")
+    nbytes, nval = KQ_BLOCK[wtype]
     _need(w, name, torch.uint8, 4)
-    if w.shape[2] * 256 != K or w.shape[3] != Q4K_BLOCK:
-        raise MoeError(3, f"{name} must be Q4_K blocks [E, R, {K // 256}, {Q4K_BLOCK}], got "
+    if w.shape[2] * nval != K or w.shape[3] != nbytes:
+        raise MoeError(3, f"{name} must be {wtype} blocks [E, R, {K // nval}, {nbytes}], got "
                           f"{tuple(w.shape)}")
 
 
+def _need_act_kind(xq, wtype):
+    want = "q8_0" if wtype == "q8_0" else "q8_k"
+    if getattr(xq, "kind", "q8_k") != want:
+        raise MoeError(3, f"{wtype} weights need {want} activations, got {xq.kind}")
+
+
 def moe_grouped_qgemm_gateup_silu(xq, w_gu, sorted_pairs, expert_offsets, K, act=None,
-                                  stream=None):
-    """xq: Q8KBuffer of x [T, H]; w_gu: Q4_K blocks uint8 [E, 2I, H/256, 144]."""
+                                  stream=None, wtype="q4_k"):
+    """xq: QBuffer of x [T, H] (the quantizer paired with wtype); w_gu: blocks
+    uint8 [E, 2I, H/values, bytes] of format wtype."""
     import torch
     T, H = xq.R, xq.K
-    _need_q4k(w_gu, "w_gu", H)
+    _need_kq(w_gu, "w_gu", H, wtype)
+    _need_act_kind(xq, wtype)
     E, I = w_gu.shape[0], w_gu.shape[1] // 2
     if sorted_pairs is not None:
         _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * K,))
@@ -396,17 +438,19 @@ def moe_grouped_qgemm_gateup_silu(xq, w_gu, sorted_pairs, expert_offsets, K, act
         act = torch.empty((T * K, I), dtype=torch.bfloat16, device=w_gu.device)
     _need(act, "act", torch.bfloat16, shape=(T * K, I))
     _check(load().moe_grouped_qgemm_gateup_silu(
-        _ptr(xq.data), T, H, _ptr(w_gu), MOE_Q4_K, E, I, _ptr(sorted_pairs),
+        _ptr(xq.data), T, H, _ptr(w_gu), MOE_QTYPE[wtype], E, I, _ptr(sorted_pairs),
         _ptr(expert_offsets), K, _ptr(act), _stream(stream)))
     return act
 
 
 def moe_grouped_qgemm_down(actq, w_d, sorted_pairs, expert_offsets, pair_w, expert_out=None,
-                           stream=None):
-    """actq: Q8KBuffer of act [P, I]; w_d: Q4_K blocks uint8 [E, H, I/256, 144]."""
+                           stream=None, wtype="q4_k"):
+    """actq: QBuffer of act [P, I]; w_d: blocks uint8 [E, H, I/values, bytes]
+    of format wtype."""
     import torch
     P, I = actq.R, actq.K
-    _need_q4k(w_d, "w_d", I)
+    _need_kq(w_d, "w_d", I, wtype)
+    _need_act_kind(actq, wtype)
     E, H = w_d.shape[0], w_d.shape[1]
     if sorted_pairs is not None:
         _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(P,))
@@ -420,7 +464,7 @@ def moe_grouped_qgemm_down(actq, w_d, sorted_pairs, expert_offsets, pair_w, expe
         expert_out = torch.empty((P, H), dtype=torch.bfloat16, device=w_d.device)
     _need(expert_out, "expert_out", torch.bfloat16, shape=(P, H))
     _check(load().moe_grouped_qgemm_down(
-        _ptr(actq.data), P, I, _ptr(w_d), MOE_Q4_K, E, H, _ptr(sorted_pairs),
+        _ptr(actq.data), P, I, _ptr(w_d), MOE_QTYPE[wtype], E, H, _ptr(sorted_pairs),
         _ptr(expert_offsets), _ptr(pair_w), _ptr(expert_out), _stream(stream)))
     return expert_out
 

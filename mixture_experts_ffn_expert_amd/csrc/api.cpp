@@ -161,7 +161,8 @@ moe_status moe_pack_weights(const uint16_t* w, int E, int R, int K, moe_pack_kin
 }
 
 // ---------------------------------------------------------------------------
-// Keep-quant path: Q8_K activation buffers and the Q4_K grouped GEMMs.
+// Keep-quant path: Q8_K / Q8_0 activation buffers and the grouped GEMMs
+// over Q4_K, Q5_K, Q6_K and Q8_0 weight blocks.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -182,6 +183,51 @@ Q8KView q8k_view(int R, int K) {
 
 bool q8k_shape_ok(int R, int K) {
   return R >= 0 && K >= 256 && K % 256 == 0 && (long long)R * K < (1LL << 31);
+}
+
+struct Q80View {
+  size_t qs, d, total;
+};
+
+Q80View q8_0_view(int R, int K) {
+  Q80View v;
+  v.qs = 0;
+  v.d = align256((size_t)R * K);
+  v.total = align256(v.d + (size_t)R * (K / 32) * 2);
+  return v;
+}
+
+bool q8_0_shape_ok(int R, int K) {
+  return R >= 0 && K >= 32 && K % 32 == 0 && (long long)R * K < (1LL << 31);
+}
+
+// bytes of one weight row of Kd values
+long long kq_row_bytes(moe_qtype wt, int Kd) {
+  switch (wt) {
+    case MOE_Q4_K: return (long long)(Kd / 256) * 144;
+    case MOE_Q5_K: return (long long)(Kd / 256) * 176;
+    case MOE_Q6_K: return (long long)(Kd / 256) * 210;
+    case MOE_Q8_0: return (long long)(Kd / 32) * 34;
+  }
+  return 0;
+}
+
+// Section pointers of an activation buffer of the format that pairs with wt.
+struct ActSections {
+  const int8_t* qs;
+  const void* d;
+  const int32_t* bs;
+};
+
+ActSections act_sections(const void* buf, moe_qtype wt, int R, int K) {
+  const unsigned char* b = static_cast<const unsigned char*>(buf);
+  if (wt == MOE_Q8_0) {
+    const Q80View v = q8_0_view(R, K);
+    return {reinterpret_cast<const int8_t*>(b + v.qs), b + v.d, nullptr};
+  }
+  const Q8KView v = q8k_view(R, K);
+  return {reinterpret_cast<const int8_t*>(b + v.qs), b + v.d,
+          reinterpret_cast<const int32_t*>(b + v.bs)};
 }
 
 }  // namespace
@@ -210,16 +256,40 @@ moe_status moe_quantize_q8k(const uint16_t* x, int R, int K, void* xq, moe_strea
                                                  static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_q8_0_bytes(int R, int K) {
+  if (!q8_0_shape_ok(R, K) || R == 0) return 0;
+  return q8_0_view(R, K).total;
+}
+
+moe_status moe_quantize_q8_0(const uint16_t* x, int R, int K, void* xq, moe_stream_t stream) {
+  const char* fn = "moe_quantize_q8_0";
+  clear_err();
+  if (!q8_0_shape_ok(R, K))
+    return fail(MOE_E_SHAPE, "%s: K=%d must be a positive multiple of 32 and R*K below 2^31 "
+                "(R=%d)", fn, K, R);
+  if (R == 0) return MOE_OK;
+  REQUIRE_PTR(fn, x);
+  REQUIRE_PTR(fn, xq);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  const Q80View v = q8_0_view(R, K);
+  unsigned char* b = static_cast<unsigned char*>(xq);
+  return hip_status(fn, moe::launch_quantize_q8_0(x, R, K, reinterpret_cast<int8_t*>(b + v.qs),
+                                                  reinterpret_cast<uint16_t*>(b + v.d),
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 static moe_status kq_common(const char* fn, moe_qtype wt, int E, int R, int Kd) {
-  if (wt != MOE_Q4_K)
-    return fail(MOE_E_DTYPE, "%s: weight type %d unsupported (only MOE_Q4_K exists)", fn,
+  if (wt != MOE_Q4_K && wt != MOE_Q5_K && wt != MOE_Q6_K && wt != MOE_Q8_0)
+    return fail(MOE_E_DTYPE,
+                "%s: weight type %d unsupported (MOE_Q8_0, MOE_Q4_K, MOE_Q5_K or MOE_Q6_K)", fn,
                 (int)wt);
   if (E < 1 || E > kMaxE) return fail(MOE_E_SHAPE, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
   if (Kd < 256 || Kd % 256)
     return fail(MOE_E_SHAPE, "%s: the reduced dimension %d must be a positive multiple of 256", fn,
                 Kd);
-  if ((long long)R * (Kd / 256) * 144 >= (1LL << 31))
-    return fail(MOE_E_SHAPE, "%s: one expert's Q4_K weights exceed 2^31 bytes", fn);
+  if ((long long)R * kq_row_bytes(wt, Kd) >= (1LL << 31))
+    return fail(MOE_E_SHAPE, "%s: one expert's weight blocks exceed 2^31 bytes", fn);
   return MOE_OK;
 }
 
@@ -250,14 +320,11 @@ moe_status moe_grouped_qgemm_gateup_silu(const void* xq, int T, int H, const voi
   REQUIRE_PTR(fn, act);
   st = check_device(fn);
   if (st != MOE_OK) return st;
-  const Q8KView v = q8k_view(T, H);
-  const unsigned char* b = static_cast<const unsigned char*>(xq);
-  return hip_status(fn, moe::launch_kq_gateup_silu(
-                            reinterpret_cast<const int8_t*>(b + v.qs),
-                            reinterpret_cast<const float*>(b + v.d),
-                            reinterpret_cast<const int32_t*>(b + v.bs), T, H,
-                            static_cast<const uint8_t*>(w_gu), E, I, sorted_pairs, expert_offsets,
-                            K, act, static_cast<hipStream_t>(stream)));
+  const ActSections a = act_sections(xq, wt, T, H);
+  return hip_status(fn, moe::launch_kq_gateup_silu(a.qs, a.d, a.bs, T, H,
+                                                   static_cast<const uint8_t*>(w_gu), (int)wt, E, I,
+                                                   sorted_pairs, expert_offsets, K, act,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_grouped_qgemm_down(const void* actq, int P, int I, const void* w_d, moe_qtype wt,
@@ -284,14 +351,10 @@ moe_status moe_grouped_qgemm_down(const void* actq, int P, int I, const void* w_
   REQUIRE_PTR(fn, expert_out);
   st = check_device(fn);
   if (st != MOE_OK) return st;
-  const Q8KView v = q8k_view(P, I);
-  const unsigned char* b = static_cast<const unsigned char*>(actq);
-  return hip_status(fn, moe::launch_kq_down(reinterpret_cast<const int8_t*>(b + v.qs),
-                                            reinterpret_cast<const float*>(b + v.d),
-                                            reinterpret_cast<const int32_t*>(b + v.bs), P, I,
-                                            static_cast<const uint8_t*>(w_d), E, H, sorted_pairs,
-                                            expert_offsets, pair_w, expert_out,
-                                            static_cast<hipStream_t>(stream)));
+  const ActSections a = act_sections(actq, wt, P, I);
+  return hip_status(fn, moe::launch_kq_down(a.qs, a.d, a.bs, P, I, static_cast<const uint8_t*>(w_d),
+                                            (int)wt, E, H, sorted_pairs, expert_offsets, pair_w,
+                                            expert_out, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,

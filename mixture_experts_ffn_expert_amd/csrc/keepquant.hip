@@ -1,23 +1,41 @@
-// keepquant.hip -- keep-quant grouped expert GEMMs on gfx950: GGUF Q4_K
-// weight blocks against Q8_K-quantized activations with an integer MFMA core
-// (PR #523 "What changed": the keep-quant expert GEMM family, Q8_K activation
-// quantizer, super-block dot products with an integer core), carrying the
-// BF16 path's epilogues: SiLU-mul after narrowing to bf16 (issue #3094 N1)
-// and the routing weight on the f32 result before its one rounding (N2).
+// keepquant.hip -- keep-quant grouped expert GEMMs on gfx950: GGUF weight
+// blocks (Q4_K, Q5_K, Q6_K, Q8_0) against activations quantized on the fly
+// (Q8_K for the K-quants, Q8_0 for Q8_0 weights) with an integer MFMA core
+// (PR #523 "What changed": the keep-quant expert GEMM family, the Q8_0 and
+// Q8_K activation quantizers, block dot products with an integer core),
+// carrying the BF16 path's epilogues: SiLU-mul after narrowing to bf16 (issue
+// #3094 N1) and the routing weight on the f32 result before its one rounding
+// (N2).
 //
-// Formats (GGUF): a Q4_K super-block holds 256 weights in 144 bytes: f16 d,
-// f16 dmin, 12 bytes of six-bit scales sc_j and mins m_j for 8 sub-blocks of
-// 32, then 128 bytes of 4-bit quants (byte b of 32-byte group i: value b of
-// sub-block 2i in the low nibble, of sub-block 2i+1 in the high nibble);
-// w = d * sc_j * q - dmin * m_j. A weight matrix [R, K] is R rows of K/256
-// super-blocks. Q8_K activations (this library's layout, moe.h): int8 quants
-// [R, K], f32 scales [R, K/256], int32 sums of 16 quants [R, K/16].
+// Formats (GGUF), per block:
+//   Q4_K, 256 values in 144 B: f16 d, f16 dmin, 12 B of six-bit scales sc_j
+//     and mins m_j (8 sub-blocks of 32), 128 B of nibbles (byte b of 32-byte
+//     group i: value b of sub-block 2i low, of sub-block 2i+1 high);
+//     w = d sc_j q - dmin m_j.
+//   Q5_K, 256 values in 176 B: as Q4_K with 32 B of high bits qh between the
+//     scales and the nibbles; value b of sub-block j adds 16 * bit j of qh[b].
+//   Q6_K, 256 values in 210 B: 128 B of low nibbles ql, 64 B of 2-bit highs
+//     qh, 16 int8 scales (sub-blocks of 16), f16 d. For half h, c < 4, l < 32
+//     the value 128h + 32c + l is the low (c < 2) or high (c >= 2) nibble of
+//     ql[64h + 32(c%2) + l] with bits 2c, 2c+1 of qh[32h + l] above it, less
+//     32; w = d sc_{v/16} q.
+//   Q8_0, 32 values in 34 B: f16 d, 32 int8 quants; w = d q.
+// Activations (this library's layouts, moe.h): Q8_K int8 [R, K], f32 scales
+// [R, K/256], int32 sums of 16 [R, K/16]; Q8_0 int8 [R, K], f16 scales
+// [R, K/32].
 //
-// Dot product of a weight row with an activation row, per super-block:
-//   d_w d_x sum_j sc_j (sum_{l in j} q4_l q8_l) - dmin_w d_x sum_j m_j bsum_j
-// Each sub-block's integer dot is one v_mfma_i32_16x16x32_i8 (16 activation
-// rows x 16 weight rows x 32 k); the scale multiply and the mins term are
-// integer; one f32 step per super-block.
+// Dot product of a weight row with an activation row per unit of 256 values
+// (one K-quant super-block, eight Q8_0 blocks):
+//   Q4_K, Q5_K: d_w d_x sum_j sc_j dot_j - dmin_w d_x sum_j m_j bsum32_j
+//   Q6_K:       d_w d_x (sum_j sc_j dot_j - 32 sum_j sc_j bsum16_j)
+//   Q8_0:       sum_b d_w,b d_x,b dot_b
+// where dot_j is the integer dot of the codes (Q6_K: the unsigned 6-bit
+// codes). One v_mfma_i32_16x16x32_i8 (16 activation rows x 16 weight rows x
+// 32 k) gives the dots of a 32-value group; Q6_K's two 16-value sub-blocks of
+// a group come from two MFMAs whose activation operand keeps one k half
+// each. The sc_j dot_j sums are integer (24-bit products); the mins and
+// offset sums are exact f32 MFMAs (16x16x4) over the activation's sub-block
+// sums; then one f32 step per unit (per block for Q8_0).
 #include "device_math.h"
 #include "launch.h"
 
@@ -25,9 +43,9 @@ namespace moe {
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x3v __attribute__((ext_vector_type(3)));
 
-constexpr int kQK = 256;        // values per super-block
-constexpr int kQ4KBytes = 144;  // bytes per Q4_K super-block
+constexpr int kQK = 256;  // values per super-block (and per unit of eight Q8_0 blocks)
 
 extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
 
@@ -87,21 +105,72 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// Q8_0 quantizer: four lanes per block of 32 (8 values each); amax over the
+// block, d = amax / 127, id = 1/d (0 when d = 0), q = round-half-away(x * id),
+// d stored as f16.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quantize_q8_0_kernel(const uint16_t* __restrict__ x,
+                                                            long long nblk,
+                                                            int8_t* __restrict__ qs,
+                                                            uint16_t* __restrict__ dq) {
+#pragma clang fp contract(off)
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long blk = t >> 2;
+  // 4 lanes of a block are consecutive; a wave holds whole blocks, so the
+  // shuffles below stay inside active lanes
+  if (blk >= nblk) return;
+  const int part = (int)(t & 3);
+  const size_t base = (size_t)blk * 32 + part * 8;
+  const uint4 raw = *reinterpret_cast<const uint4*>(x + base);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const float d = __fdiv_rn(amax, 127.0f);
+  const float id = (d != 0.0f) ? __fdiv_rn(1.0f, d) : 0.0f;
+  uint32_t packed[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = (int)__builtin_roundf(v[i] * id);  // half away from zero
+    packed[i >> 2] |= (uint32_t)(q & 0xFF) << (8 * (i & 3));
+  }
+  *reinterpret_cast<uint2*>(qs + base) = make_uint2(packed[0], packed[1]);
+  if (part == 0) dq[blk] = __builtin_bit_cast(uint16_t, (_Float16)d);
+}
+
+// ---------------------------------------------------------------------------
 // Grouped keep-quant GEMM, few rows per expert (decode): one workgroup = one
 // 16-row tile of one expert x 16*NFO output columns (gate-up: each group of
-// 16 gate rows with the 16 matching up rows); its KS waves split the
-// super-blocks and add their partial f32 tiles in LDS in a fixed order. The
-// activation side of a super-block (A operands, scales, sums) is loaded once
-// per wave and used by all its weight fragments.
+// 16 gate rows with the 16 matching up rows); its KS waves split the units of
+// 256 values and add their partial f32 tiles in LDS in a fixed order. The
+// activation side of a unit is loaded once per wave and used by all its
+// weight fragments; every fragment's weight loads are issued before the
+// first MFMA of the unit.
 // ---------------------------------------------------------------------------
+enum { KQ_Q8_0 = 8, KQ_Q4_K = 12, KQ_Q5_K = 13, KQ_Q6_K = 14 };
+
+// bytes per unit of 256 values
+template <int FMT>
+constexpr int kq_unit_bytes() {
+  return FMT == KQ_Q4_K ? 144 : FMT == KQ_Q5_K ? 176 : FMT == KQ_Q6_K ? 210 : 272;
+}
+
 struct KqArgs {
   const int8_t* xq;        // activation quants [a_rows, kdim]
-  const float* xd;         // activation scales [a_rows, kdim / 256]
-  const int32_t* xs;       // activation sums of 16 [a_rows, kdim / 16]
+  const void* xd;          // activation scales: f32 [a_rows, kdim/256] or f16 [a_rows, kdim/32]
+  const int32_t* xs;       // activation sums of 16 [a_rows, kdim / 16] (Q8_K only)
   int a_rows;
   const int32_t* sorted;   // sorted pair ids, or null
   int gather_k;            // >0: activation row = sorted[q] / gather_k; 0: row q
-  const uint8_t* W;        // Q4_K weights [E, b_rows, kdim / 256, 144]
+  const uint8_t* W;        // weight blocks [E, b_rows, kdim / 256 units]
   int b_rows;              // 2I (gate-up) or H (down)
   const int32_t* offsets;  // [E+1] or null
   int E, P, kdim, n_out;
@@ -169,11 +238,268 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kq_rsrc(const void* base, size
 
 constexpr uint32_t kqOob = 0x80000000u;
 
-template <int EPI, int KS, int NFO>
+// 8 bytes at a 2-aligned offset: one dword-aligned 12-byte load, realigned
+// (the load starts at most 2 bytes before off and ends 4 bytes after off+7)
+__device__ __forceinline__ uint2 kq_load8_a2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const uint32_t sh = off & 3u;
+  const u32x3v w = __builtin_bit_cast(u32x3v, __builtin_amdgcn_raw_buffer_load_b96(r, off - sh, 0, 0));
+  return make_uint2(__builtin_amdgcn_alignbyte(w.y, w.x, sh), __builtin_amdgcn_alignbyte(w.z, w.y, sh));
+}
+
+__device__ __forceinline__ uint2 kq_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+__device__ __forceinline__ long kq_pair(uint32_t lo, uint32_t hi) {
+  return (long)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ float kq_f16(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+}
+
+// Weight registers of one 16-row fragment for one unit, per format.
+template <int FMT>
+struct KqW;
+template <>
+struct KqW<KQ_Q4_K> {
+  i32x4v hdr;
+  uint2 qs[4];
+};
+template <>
+struct KqW<KQ_Q5_K> {
+  i32x4v hdr;
+  uint2 qh;
+  uint2 qs[4];
+};
+template <>
+struct KqW<KQ_Q6_K> {
+  uint2 ql[4];   // (half h, column pair c2): index 2h + c2
+  uint2 qh[2];
+  i32x4v sc;     // 16 scale bytes, dword-aligned copy of offsets 192 - sh ..
+  uint32_t sc_tail, dbits, sh;
+};
+template <>
+struct KqW<KQ_Q8_0> {
+  uint2 q[8];
+  uint32_t d[8];
+};
+
+// Loads the unit at byte offset `base` (kqOob-based offsets stay out of
+// range) of this lane's weight row; lane chunk kc of every 32-value group.
+template <int FMT>
+__device__ __forceinline__ void kq_wload(KqW<FMT>& w, __amdgpu_buffer_rsrc_t r, uint32_t base,
+                                         int kc) {
+  if constexpr (FMT == KQ_Q4_K) {
+    w.hdr = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, base, 0, 0));
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w.qs[p] = kq_load8(r, base + 16 + p * 32 + kc * 8);
+  } else if constexpr (FMT == KQ_Q5_K) {
+    w.hdr = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, base, 0, 0));
+    w.qh = kq_load8(r, base + 16 + kc * 8);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w.qs[p] = kq_load8(r, base + 48 + p * 32 + kc * 8);
+  } else if constexpr (FMT == KQ_Q6_K) {
+    // 210-byte blocks: base is 2-aligned; every load stays in [base - 2,
+    // base + 210)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) w.ql[2 * h + c2] = kq_load8_a2(r, base + 64 * h + 32 * c2 + kc * 8);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) w.qh[h] = kq_load8_a2(r, base + 128 + 32 * h + kc * 8);
+    w.sh = base & 3u;
+    w.sc = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, base + 192 - w.sh, 0, 0));
+    w.sc_tail = __builtin_amdgcn_raw_buffer_load_b16(r, base + 206, 0, 0);
+    w.dbits = __builtin_amdgcn_raw_buffer_load_b16(r, base + 208, 0, 0);
+  } else {
+    // eight 34-byte blocks; base is 4-aligned (rows of 272-byte units), so
+    // the quants of even blocks sit 2 bytes past a dword boundary
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint32_t qo = base + 34 * b + 2 + kc * 8;
+      w.q[b] = (b & 1) ? kq_load8(r, qo) : kq_load8_a2(r, qo);
+      w.d[b] = __builtin_amdgcn_raw_buffer_load_b16(r, base + 34 * b, 0, 0);
+    }
+  }
+}
+
+// Activation registers of one unit, per activation format.
+template <int FMT>
+struct KqA {
+  long aop[8];      // A operands of the 8 groups of 32 (this lane's row r16, chunk kc)
+  float bsa[4];     // A operands of the mins / offset MFMAs
+  float dx[4][8];   // scales of the 4 C rows (K-quants: [i][0]; Q8_0: per block)
+};
+
+template <int FMT>
+__device__ __forceinline__ void kq_aload(KqA<FMT>& a, const KqArgs& g,
+                                         __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rd,
+                                         __amdgpu_buffer_rsrc_t rs, int arow, const int* crow,
+                                         int u, int kc) {
+  const uint32_t aq = (arow >= 0) ? (uint32_t)arow * (uint32_t)g.kdim + u * kQK + kc * 8 : kqOob;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a.aop[j] = (long)__builtin_bit_cast(uint64_t, kq_load8(rq, aq + j * 32));
+  const int nsb = g.kdim / kQK;
+  if constexpr (FMT == KQ_Q8_0) {
+    // 8 f16 scales per row and unit: one 16-byte load per C row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = (crow[i] >= 0) ? ((uint32_t)crow[i] * (g.kdim / 32) + u * 8) * 2 : kqOob;
+      const i32x4v h = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(rd, o, 0, 0));
+      const uint32_t hw[4] = {(uint32_t)h.x, (uint32_t)h.y, (uint32_t)h.z, (uint32_t)h.w};
+#pragma unroll
+      for (int b = 0; b < 8; ++b) a.dx[i][b] = kq_f16(hw[b >> 1] >> (16 * (b & 1)));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = (crow[i] >= 0) ? ((uint32_t)crow[i] * nsb + u) * 4 : kqOob;
+      a.dx[i][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o, 0, 0));
+    }
+    const uint32_t so = (arow >= 0) ? ((uint32_t)arow * (g.kdim / 16) + u * 16) * 4 : kqOob;
+    if constexpr (FMT == KQ_Q6_K) {
+      // sums of 16 of sub-blocks 4m + kc
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        a.bsa[m] = (float)(int)__builtin_amdgcn_raw_buffer_load_b32(rs, so + (4 * m + kc) * 4, 0, 0);
+    } else {
+      // sums of 32 of sub-blocks kc and kc + 4
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint2 s2 = kq_load8(rs, so + 2 * (kc + 4 * h) * 4);
+        a.bsa[h] = (float)((int)s2.x + (int)s2.y);
+      }
+    }
+  }
+}
+
+// Scales and mins of a Q4_K / Q5_K header for this lane's column.
+__device__ __forceinline__ void kq_scales_k4(const i32x4v hdr, int kc, int* sc, float& mnb0,
+                                             float& mnb1) {
+  // bytes 0-3 (low 6 bits) give sc_0..3; bytes 8-11 (low nibble) with the
+  // top 2 bits of bytes 0-3 give sc_4..7
+  const uint32_t b03 = (uint32_t)hdr.y, b47 = (uint32_t)hdr.z, b811 = (uint32_t)hdr.w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = (b03 >> (8 * j)) & 63;
+    sc[j + 4] = ((b811 >> (8 * j)) & 0xF) | (((b03 >> (8 * j + 6)) & 3) << 4);
+  }
+  // B operands of the mins MFMAs: m_kc and m_kc+4 (bytes 4-7 low 6 bits;
+  // bytes 8-11 high nibble with the top 2 bits of bytes 4-7)
+  const uint32_t sh = 8u * (uint32_t)kc;
+  mnb0 = (float)((b47 >> sh) & 63);
+  mnb1 = (float)(((b811 >> (sh + 4)) & 0xF) | (((b47 >> (sh + 6)) & 3) << 4));
+}
+
+// One fragment's contribution for one unit: acc[i] (C row kc*4 + i, this
+// lane's column) += the unit's dot product.
+template <int FMT>
+__device__ __forceinline__ void kq_frag(float* acc, const KqW<FMT>& w, const KqA<FMT>& a,
+                                        const long* alo, const long* ahi, int kc) {
+#pragma clang fp contract(off)
+  const i32x4v z = {0, 0, 0, 0};
+  const f32x4v zf = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr uint32_t M4 = 0x0F0F0F0Fu;
+  if constexpr (FMT == KQ_Q4_K || FMT == KQ_Q5_K) {
+    const float dw = kq_f16((uint32_t)w.hdr.x);
+    const float dmw = kq_f16((uint32_t)w.hdr.x >> 16);
+    int sc[8];
+    float mnb0, mnb1;
+    kq_scales_k4(w.hdr, kc, sc, mnb0, mnb1);
+    int sumi[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int j = 2 * p + half;
+        uint32_t lo = half ? ((w.qs[p].x >> 4) & M4) : (w.qs[p].x & M4);
+        uint32_t hi = half ? ((w.qs[p].y >> 4) & M4) : (w.qs[p].y & M4);
+        if constexpr (FMT == KQ_Q5_K) {
+          // bit j of each qh byte -> bit 4 of the code
+          lo |= ((w.qh.x >> j) & 0x01010101u) << 4;
+          hi |= ((w.qh.y >> j) & 0x01010101u) << 4;
+        }
+        const i32x4v dot = __builtin_amdgcn_mfma_i32_16x16x32_i8(a.aop[j], kq_pair(lo, hi), z, 0, 0, 0);
+        // |dot| <= 32 * 31 * 127 and sc_j <= 63: 24-bit operands
+        sumi[0] += __mul24(sc[j], dot.x);
+        sumi[1] += __mul24(sc[j], dot.y);
+        sumi[2] += __mul24(sc[j], dot.z);
+        sumi[3] += __mul24(sc[j], dot.w);
+      }
+    }
+    // mins term sum_j m_j bsum32_j of the 4 C rows: integers below 2^22
+    f32x4v summ = __builtin_amdgcn_mfma_f32_16x16x4f32(a.bsa[0], mnb0, zf, 0, 0, 0);
+    summ = __builtin_amdgcn_mfma_f32_16x16x4f32(a.bsa[1], mnb1, summ, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float dall = dw * a.dx[i][0];
+      const float dmn = dmw * a.dx[i][0];
+      const float t1 = dall * (float)sumi[i];
+      const float t2 = dmn * summ[i];
+      acc[i] = acc[i] + (t1 - t2);
+    }
+  } else if constexpr (FMT == KQ_Q6_K) {
+    const float dw = kq_f16(w.dbits);
+    // the 16 scale bytes, realigned: s[m] holds scales 4m .. 4m+3
+    const uint32_t s[4] = {
+        __builtin_amdgcn_alignbyte((uint32_t)w.sc.y, (uint32_t)w.sc.x, w.sh),
+        __builtin_amdgcn_alignbyte((uint32_t)w.sc.z, (uint32_t)w.sc.y, w.sh),
+        __builtin_amdgcn_alignbyte((uint32_t)w.sc.w, (uint32_t)w.sc.z, w.sh),
+        __builtin_amdgcn_alignbyte(w.sc_tail, (uint32_t)w.sc.w, w.sh)};
+    int sumi[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int grp = 0; grp < 8; ++grp) {
+      const int h = grp >> 2, c = grp & 3;
+      const uint2 ql = w.ql[2 * h + (c & 1)];
+      const uint2 qh = w.qh[h];
+      const uint32_t lo = ((c < 2 ? ql.x : (ql.x >> 4)) & M4) | (((qh.x >> (2 * c)) & 0x03030303u) << 4);
+      const uint32_t hi = ((c < 2 ? ql.y : (ql.y >> 4)) & M4) | (((qh.y >> (2 * c)) & 0x03030303u) << 4);
+      const long bop = kq_pair(lo, hi);
+      // sub-blocks 2 grp (k 0-15 of the group) and 2 grp + 1 (k 16-31)
+      const i32x4v da = __builtin_amdgcn_mfma_i32_16x16x32_i8(alo[grp], bop, z, 0, 0, 0);
+      const i32x4v db = __builtin_amdgcn_mfma_i32_16x16x32_i8(ahi[grp], bop, z, 0, 0, 0);
+      const int j = 2 * grp;
+      const int sa = (int)(s[j >> 2] << (24 - 8 * (j & 3))) >> 24;
+      const int sb = (int)(s[(j + 1) >> 2] << (24 - 8 * ((j + 1) & 3))) >> 24;
+      // |dot| <= 16 * 63 * 127, |sc| <= 128: 24-bit operands
+      sumi[0] += __mul24(sa, da.x) + __mul24(sb, db.x);
+      sumi[1] += __mul24(sa, da.y) + __mul24(sb, db.y);
+      sumi[2] += __mul24(sa, da.z) + __mul24(sb, db.z);
+      sumi[3] += __mul24(sa, da.w) + __mul24(sb, db.w);
+    }
+    // offset term sum_j sc_j bsum16_j: integers below 2^23, exact in f32
+    f32x4v so = zf;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float scb = (float)((int)(s[m] << (24 - 8 * kc)) >> 24);
+      so = __builtin_amdgcn_mfma_f32_16x16x4f32(a.bsa[m], scb, so, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int total = sumi[i] - 32 * (int)so[i];
+      acc[i] = acc[i] + (dw * a.dx[i][0]) * (float)total;
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const i32x4v dot =
+          __builtin_amdgcn_mfma_i32_16x16x32_i8(a.aop[b], kq_pair(w.q[b].x, w.q[b].y), z, 0, 0, 0);
+      const float dw = kq_f16(w.d[b]);
+      acc[0] = acc[0] + (dw * a.dx[0][b]) * (float)dot.x;
+      acc[1] = acc[1] + (dw * a.dx[1][b]) * (float)dot.y;
+      acc[2] = acc[2] + (dw * a.dx[2][b]) * (float)dot.z;
+      acc[3] = acc[3] + (dw * a.dx[3][b]) * (float)dot.w;
+    }
+  }
+}
+
+template <int EPI, int FMT, int KS, int NFO>
 __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
 #pragma clang fp contract(off)
   // weight fragments of 16 rows: NFO column groups, each gate (and up)
   constexpr int NB = (EPI == KQ_GATEUP) ? 2 * NFO : NFO;
+  constexpr int UB = kq_unit_bytes<FMT>();
   __shared__ float red[KS][NB][4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -183,7 +509,7 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
   if (!kq_find_tile(g, slot, e, row0, rows)) return;  // uniform over the workgroup
   const int col0 = nb * 16 * NFO;
   const int r16 = lane & 15;   // A row / B column of this lane's MFMA operands
-  const int kc = lane >> 4;    // 8-value k chunk of a 32-value sub-block
+  const int kc = lane >> 4;    // 8-value k chunk of a 32-value group
   const int nsb = g.kdim / kQK;
 
   // activation row of this lane's A operand, and of its 4 C rows
@@ -204,14 +530,16 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
 
   const size_t a_rows = (size_t)g.a_rows;
   const __amdgpu_buffer_rsrc_t rq = kq_rsrc(g.xq, a_rows * g.kdim);
-  const __amdgpu_buffer_rsrc_t rd = kq_rsrc(g.xd, a_rows * nsb * 4);
-  const __amdgpu_buffer_rsrc_t rs = kq_rsrc(g.xs, a_rows * (g.kdim / 16) * 4);
-  const size_t row_bytes = (size_t)nsb * kQ4KBytes;
+  const __amdgpu_buffer_rsrc_t rd =
+      kq_rsrc(g.xd, FMT == KQ_Q8_0 ? a_rows * (g.kdim / 32) * 2 : a_rows * nsb * 4);
+  const __amdgpu_buffer_rsrc_t rs =
+      kq_rsrc(g.xs, FMT == KQ_Q8_0 ? 0 : a_rows * (g.kdim / 16) * 4);
+  const size_t row_bytes = (size_t)nsb * UB;
   const __amdgpu_buffer_rsrc_t rw =
       kq_rsrc(g.W + (size_t)e * g.b_rows * row_bytes, (size_t)g.b_rows * row_bytes);
 
-  // byte offsets (super-block 0) of this lane's weight rows: fragment f is
-  // column group f / 2 (gate-up: f even gate, f odd up) or f (down)
+  // byte offsets (unit 0) of this lane's weight rows: fragment f is column
+  // group f / 2 (gate-up: f even gate, f odd up) or f (down)
   uint32_t wrow[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f) {
@@ -220,7 +548,6 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
     const int wr = (EPI == KQ_GATEUP && (f & 1)) ? g.n_out + c : c;
     wrow[f] = (c < g.n_out) ? (uint32_t)(wr * row_bytes) : kqOob;
   }
-  const uint32_t aq_off = (arow >= 0) ? (uint32_t)((size_t)arow * g.kdim) + kc * 8 : kqOob;
 
   float acc[NB][4];
 #pragma unroll
@@ -228,106 +555,30 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[f][i] = 0.0f;
 
-  // this wave's super-blocks
+  // this wave's units
   const int per = (nsb + KS - 1) / KS;
-  const int sb0 = min(nsb, wave * per), sb1 = min(nsb, sb0 + per);
-  for (int sb = sb0; sb < sb1; ++sb) {
-    // activation side, shared by every fragment: A operands of the 8
-    // sub-blocks, sub-block sums, and the scales of the 4 C rows
-    long aop[8];
+  const int u0 = min(nsb, wave * per), u1 = min(nsb, u0 + per);
+  for (int u = u0; u < u1; ++u) {
+    KqA<FMT> a;
+    kq_aload<FMT>(a, g, rq, rd, rs, arow, crow, u, kc);
+    // Q6_K: activation operands restricted to k 0-15 / 16-31 of each group
+    long alo[8], ahi[8];
+    if constexpr (FMT == KQ_Q6_K) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t ao = (aq_off == kqOob) ? kqOob : aq_off + sb * kQK + j * 32;
-      aop[j] = (long)__builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rq, ao, 0, 0));
-    }
-    // A operands of the mins term: sums of the 32 quants of sub-blocks kc
-    // and kc + 4 of activation row r16
-    float bsa[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t so =
-          (arow < 0) ? kqOob : (uint32_t)(arow * (g.kdim / 16) + sb * 16 + 2 * (kc + 4 * h)) * 4;
-      const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, so, 0, 0));
-      bsa[h] = (float)((int)s2.x + (int)s2.y);
-    }
-    float dx[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t ro = (crow[i] >= 0) ? (uint32_t)(crow[i] * nsb + sb) * 4 : kqOob;
-      dx[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, ro, 0, 0));
-    }
-    // every fragment's weight loads first (headers: f16 d, f16 dmin, 12
-    // bytes of six-bit scales and mins; then the quants), so that the
-    // whole super-block is in flight before the first MFMA
-    const uint32_t sboff = (uint32_t)sb * kQ4KBytes;
-    i32x4v hdrs[NB];
-    uint2 w8s[NB][4];
-#pragma unroll
-    for (int f = 0; f < NB; ++f) {
-      const uint32_t ho = (wrow[f] == kqOob) ? kqOob : wrow[f] + sboff;
-      hdrs[f] = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(rw, ho, 0, 0));
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t qo = (ho == kqOob) ? kqOob : ho + 16 + p * 32 + kc * 8;
-        w8s[f][p] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rw, qo, 0, 0));
+      for (int j = 0; j < 8; ++j) {
+        alo[j] = (kc < 2) ? a.aop[j] : 0;
+        ahi[j] = (kc < 2) ? 0 : a.aop[j];
       }
     }
+    KqW<FMT> w[NB];
+#pragma unroll
+    for (int f = 0; f < NB; ++f) kq_wload<FMT>(w[f], rw, wrow[f] + (uint32_t)u * UB, kc);
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
       // one fragment at a time: keeps the MFMA results of only one
       // fragment live
       __builtin_amdgcn_sched_barrier(0);
-      const i32x4v hdr = hdrs[f];
-      const uint2* w8 = w8s[f];
-      const float dw = (float)__builtin_bit_cast(_Float16, (uint16_t)(hdr.x & 0xFFFF));
-      const float dmw = (float)__builtin_bit_cast(_Float16, (uint16_t)((uint32_t)hdr.x >> 16));
-      // scales of the 8 sub-blocks: bytes 0-3 (low 6 bits) give sc_0..3;
-      // bytes 8-11 (low nibble) with the top 2 bits of bytes 0-3 give sc_4..7
-      const uint32_t b03 = (uint32_t)hdr.y, b47 = (uint32_t)hdr.z, b811 = (uint32_t)hdr.w;
-      int sc[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sc[j] = (b03 >> (8 * j)) & 63;
-        sc[j + 4] = ((b811 >> (8 * j)) & 0xF) | (((b03 >> (8 * j + 6)) & 3) << 4);
-      }
-      // B operands of the mins term: m_kc and m_kc+4 of this lane's column
-      // (bytes 4-7 low 6 bits; bytes 8-11 high nibble with the top 2 bits
-      // of bytes 4-7)
-      const uint32_t sh = 8u * (uint32_t)kc;
-      const float mnb0 = (float)((b47 >> sh) & 63);
-      const float mnb1 = (float)(((b811 >> (sh + 4)) & 0xF) | (((b47 >> (sh + 6)) & 3) << 4));
-      // integer sub-block dots, scaled by sc_j (this lane's column)
-      int sumi[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int j = 2 * p + half;
-          const uint32_t lo = half ? ((w8[p].x >> 4) & 0x0F0F0F0Fu) : (w8[p].x & 0x0F0F0F0Fu);
-          const uint32_t hi = half ? ((w8[p].y >> 4) & 0x0F0F0F0Fu) : (w8[p].y & 0x0F0F0F0Fu);
-          const long bop = (long)(((uint64_t)hi << 32) | lo);
-          const i32x4v z = {0, 0, 0, 0};
-          const i32x4v dot = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[j], bop, z, 0, 0, 0);
-          // |dot| <= 32 * 15 * 127 and sc_j <= 63: 24-bit products suffice
-          sumi[0] += __mul24(sc[j], dot.x);
-          sumi[1] += __mul24(sc[j], dot.y);
-          sumi[2] += __mul24(sc[j], dot.z);
-          sumi[3] += __mul24(sc[j], dot.w);
-        }
-      }
-      // mins term sum_j m_j bsum_j of the 4 C rows: integers below 2^21,
-      // exact in f32
-      const f32x4v zf = {0.0f, 0.0f, 0.0f, 0.0f};
-      f32x4v summ = __builtin_amdgcn_mfma_f32_16x16x4f32(bsa[0], mnb0, zf, 0, 0, 0);
-      summ = __builtin_amdgcn_mfma_f32_16x16x4f32(bsa[1], mnb1, summ, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float dall = dw * dx[i];
-        const float dmn = dmw * dx[i];
-        const float t1 = dall * (float)sumi[i];
-        const float t2 = dmn * summ[i];
-        acc[f][i] = acc[f][i] + (t1 - t2);
-      }
+      kq_frag<FMT>(acc[f], w[f], a, alo, ahi, kc);
     }
   }
 
@@ -383,41 +634,64 @@ hipError_t launch_quantize_q8k(const uint16_t* x, int R, int K, int8_t* qs, floa
   return hipGetLastError();
 }
 
-template <int EPI, int KS, int NFO>
+hipError_t launch_quantize_q8_0(const uint16_t* x, int R, int K, int8_t* qs, uint16_t* d,
+                                hipStream_t s) {
+  const long long nblk = (long long)R * (K / 32);
+  const long long threads = nblk * 4;
+  hipLaunchKernelGGL(quantize_q8_0_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     s, x, nblk, qs, d);
+  return hipGetLastError();
+}
+
+template <int EPI, int FMT, int KS, int NFO>
 static hipError_t kq_launch_shape(KqArgs g, hipStream_t s) {
   g.nblk = (g.n_out + 16 * NFO - 1) / (16 * NFO);
   g.slots = kq_slots(g.P, g.E, g.offsets != nullptr);
   const unsigned grid = (unsigned)((long long)g.slots * g.nblk);
   void* args[] = {&g};
-  return timed_launch(reinterpret_cast<const void*>(kq_stream_kernel<EPI, KS, NFO>), dim3(grid),
-                      dim3(64 * KS), args, s);
+  return timed_launch(reinterpret_cast<const void*>(kq_stream_kernel<EPI, FMT, KS, NFO>),
+                      dim3(grid), dim3(64 * KS), args, s);
 }
 
-// k split over as many waves as there are super-blocks (at most 4); 64
-// output columns per workgroup
-template <int EPI>
-static hipError_t kq_launch(KqArgs g, hipStream_t s) {
+// k split over as many waves as there are units (at most 4); 64 output
+// columns per workgroup for the 4-bit and 5-bit formats, 32 for the wider
+// ones (whose fragments hold more weight registers)
+template <int EPI, int FMT>
+static hipError_t kq_launch_fmt(KqArgs g, hipStream_t s) {
+  constexpr int NFO = (FMT == KQ_Q4_K || FMT == KQ_Q5_K) ? 4 : 2;
   const int nsb = g.kdim / kQK;
-  if (nsb >= 4) return kq_launch_shape<EPI, 4, 4>(g, s);
-  if (nsb == 3) return kq_launch_shape<EPI, 3, 4>(g, s);
-  if (nsb == 2) return kq_launch_shape<EPI, 2, 4>(g, s);
-  return kq_launch_shape<EPI, 1, 4>(g, s);
+  if (nsb >= 4) return kq_launch_shape<EPI, FMT, 4, NFO>(g, s);
+  if (nsb == 3) return kq_launch_shape<EPI, FMT, 3, NFO>(g, s);
+  if (nsb == 2) return kq_launch_shape<EPI, FMT, 2, NFO>(g, s);
+  return kq_launch_shape<EPI, FMT, 1, NFO>(g, s);
 }
 
-hipError_t launch_kq_gateup_silu(const int8_t* xq, const float* xd, const int32_t* xs, int T, int H,
-                                 const uint8_t* w_gu, int E, int I, const int32_t* sorted,
-                                 const int32_t* offsets, int K, uint16_t* act, hipStream_t s) {
+template <int EPI>
+static hipError_t kq_launch(KqArgs g, int wtype, hipStream_t s) {
+  switch (wtype) {
+    case KQ_Q4_K: return kq_launch_fmt<EPI, KQ_Q4_K>(g, s);
+    case KQ_Q5_K: return kq_launch_fmt<EPI, KQ_Q5_K>(g, s);
+    case KQ_Q6_K: return kq_launch_fmt<EPI, KQ_Q6_K>(g, s);
+    case KQ_Q8_0: return kq_launch_fmt<EPI, KQ_Q8_0>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_kq_gateup_silu(const int8_t* xq, const void* xd, const int32_t* xs, int T, int H,
+                                 const uint8_t* w_gu, int wtype, int E, int I,
+                                 const int32_t* sorted, const int32_t* offsets, int K,
+                                 uint16_t* act, hipStream_t s) {
   KqArgs g{};
   g.xq = xq; g.xd = xd; g.xs = xs; g.a_rows = T;
   g.sorted = sorted; g.gather_k = K;
   g.W = w_gu; g.b_rows = 2 * I;
   g.offsets = offsets; g.E = E; g.P = T * K; g.kdim = H; g.n_out = I;
   g.out = act;
-  return kq_launch<KQ_GATEUP>(g, s);
+  return kq_launch<KQ_GATEUP>(g, wtype, s);
 }
 
-hipError_t launch_kq_down(const int8_t* aq, const float* ad, const int32_t* as, int P, int I,
-                          const uint8_t* w_d, int E, int H, const int32_t* sorted,
+hipError_t launch_kq_down(const int8_t* aq, const void* ad, const int32_t* as, int P, int I,
+                          const uint8_t* w_d, int wtype, int E, int H, const int32_t* sorted,
                           const int32_t* offsets, const float* pair_w, uint16_t* out,
                           hipStream_t s) {
   KqArgs g{};
@@ -426,7 +700,7 @@ hipError_t launch_kq_down(const int8_t* aq, const float* ad, const int32_t* as, 
   g.W = w_d; g.b_rows = H;
   g.offsets = offsets; g.E = E; g.P = P; g.kdim = I; g.n_out = H;
   g.out = out; g.pair_w = pair_w;
-  return kq_launch<KQ_DOWN>(g, s);
+  return kq_launch<KQ_DOWN>(g, wtype, s);
 }
 
 }  // namespace moe

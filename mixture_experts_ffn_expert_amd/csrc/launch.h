@@ -55,11 +55,16 @@ hipError_t launch_combine(const void* eo, int eo_bf16, int T, int K, int H, cons
 // keepquant.hip
 hipError_t launch_quantize_q8k(const uint16_t* x, int R, int K, int8_t* qs, float* d,
                                int32_t* bsums, hipStream_t s);
-hipError_t launch_kq_gateup_silu(const int8_t* xq, const float* xd, const int32_t* xs, int T, int H,
-                                 const uint8_t* w_gu, int E, int I, const int32_t* sorted,
-                                 const int32_t* offsets, int K, uint16_t* act, hipStream_t s);
-hipError_t launch_kq_down(const int8_t* aq, const float* ad, const int32_t* as, int P, int I,
-                          const uint8_t* w_d, int E, int H, const int32_t* sorted,
+hipError_t launch_quantize_q8_0(const uint16_t* x, int R, int K, int8_t* qs, uint16_t* d,
+                                hipStream_t s);
+// wtype: GGUF type id (8 = Q8_0, 12 = Q4_K, 13 = Q5_K, 14 = Q6_K); xd points at
+// f32 Q8_K scales or f16 Q8_0 scales; xs (Q8_K sums of 16) is unused for Q8_0
+hipError_t launch_kq_gateup_silu(const int8_t* xq, const void* xd, const int32_t* xs, int T, int H,
+                                 const uint8_t* w_gu, int wtype, int E, int I,
+                                 const int32_t* sorted, const int32_t* offsets, int K,
+                                 uint16_t* act, hipStream_t s);
+hipError_t launch_kq_down(const int8_t* aq, const void* ad, const int32_t* as, int P, int I,
+                          const uint8_t* w_d, int wtype, int E, int H, const int32_t* sorted,
                           const int32_t* offsets, const float* pair_w, uint16_t* out,
                           hipStream_t s);
 

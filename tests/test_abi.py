@@ -224,3 +224,16 @@ def test_keepquant_refusals(lib):
     assert d(A, 8, 300, A2, 12, 8, 512, A, A, None, A, None) == 3
     assert d(A, 8, 256, A2, 12, 2, 512, None, None, None, A, None) == 1 and "E=1" in _err(lib)
     assert q(None, 0, 512, None, 12, 8, 256, A, A, 2, None, None) == 0
+    for wt in (8, 13, 14):                                    # the other formats pass validation
+        assert q(None, 0, 512, None, wt, 8, 256, A, A, 2, None, None) == 0
+        assert q(A, 4, 300, A2, wt, 8, 256, A, A, 2, A, None) == 3 and "256" in _err(lib)
+    assert q(A, 4, 512, A2, 15, 8, 256, A, A, 2, A, None) == 2 and "MOE_Q6_K" in _err(lib)
+
+
+def test_q8_0_buffer_and_refusals(lib):
+    assert lib.moe_q8_0_bytes(4, 40) == 0 and lib.moe_q8_0_bytes(0, 64) == 0
+    assert lib.moe_q8_0_bytes(4, 512) == 2048 + 256             # quants, f16 scales (aligned)
+    assert lib.moe_q8_0_bytes(3, 96) == 512 + 256               # 288 quant bytes, 18 scale bytes
+    assert lib.moe_quantize_q8_0(A, 4, 40, A2, None) == 3 and "32" in _err(lib)
+    assert lib.moe_quantize_q8_0(None, 0, 64, None, None) == 0
+    assert lib.moe_quantize_q8_0(MIS, 4, 64, A2, None) == 1 and "aligned" in _err(lib)
