@@ -653,17 +653,21 @@ static hipError_t kq_launch_shape(KqArgs g, hipStream_t s) {
                       dim3(grid), dim3(64 * KS), args, s);
 }
 
-// k split over as many waves as there are units (at most 4); 64 output
-// columns per workgroup for the 4-bit and 5-bit formats, 32 for the wider
-// ones (whose fragments hold more weight registers)
+// 32 output columns per workgroup. Gate-up (H units of 256, two weight rows
+// per column) splits k over up to 4 waves; down (fewer units, twice the
+// columns) gives each workgroup one wave and all the units, which measured
+// faster on the decode shapes.
 template <int EPI, int FMT>
 static hipError_t kq_launch_fmt(KqArgs g, hipStream_t s) {
-  constexpr int NFO = (FMT == KQ_Q4_K || FMT == KQ_Q5_K) ? 4 : 2;
-  const int nsb = g.kdim / kQK;
-  if (nsb >= 4) return kq_launch_shape<EPI, FMT, 4, NFO>(g, s);
-  if (nsb == 3) return kq_launch_shape<EPI, FMT, 3, NFO>(g, s);
-  if (nsb == 2) return kq_launch_shape<EPI, FMT, 2, NFO>(g, s);
-  return kq_launch_shape<EPI, FMT, 1, NFO>(g, s);
+  if constexpr (EPI == KQ_DOWN) {
+    return kq_launch_shape<EPI, FMT, 1, 2>(g, s);
+  } else {
+    const int nsb = g.kdim / kQK;
+    if (nsb >= 4) return kq_launch_shape<EPI, FMT, 4, 2>(g, s);
+    if (nsb == 3) return kq_launch_shape<EPI, FMT, 3, 2>(g, s);
+    if (nsb == 2) return kq_launch_shape<EPI, FMT, 2, 2>(g, s);
+    return kq_launch_shape<EPI, FMT, 1, 2>(g, s);
+  }
 }
 
 template <int EPI>
