@@ -143,6 +143,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the extra timing of the layer with the fused expert FFN")
     ap.add_argument("--layers", type=int, default=2,
                     help="distinct weight sets (layers) the steps cycle through, so that no "
                          "step finds its weights in the 256 MB last-level cache (default 2)")
@@ -226,7 +228,15 @@ def main():
         e.record(stream)
         return e
 
-    def step(record, lw):
+    # the decode shapes also time the layer with the fused expert FFN
+    # (moe_fused_expert_ffn) in place of the two GEMM calls
+    fused_ok = (not keepquant) and T * K <= 8 * E and not args.no_fused
+    ws_f = None
+    if fused_ok:
+        nws = moe.moe_fused_expert_ffn_workspace_bytes(T, E, K, True) // 4
+        ws_f = torch.zeros((nws,), dtype=torch.int32, device=dev)
+
+    def step(record, lw, fused=False):
         w_r, w_gu, w_d = lw["w_r"], lw["w_gu"], lw["w_d"]
         w_gu_s, w_d_s, w_g = lw.get("w_gu_s"), lw.get("w_d_s"), lw.get("w_g")
         logits = moe.moe_router_logits(x, w_r, bias, bufs.get("logits"))
@@ -248,22 +258,28 @@ def main():
             # added to the queue), on the stream they run on
             evs = record
             moe.moe_time_next_gemm(evs[0], evs[1])
-        if keepquant:
+        if fused:
+            act, eo = moe.moe_fused_expert_ffn(x, w_gu, w_d, sp, off, K, w, ws_f,
+                                               bufs.get("act"), bufs.get("expert_out"))
+            if record:
+                ev.append(evs)
+        elif keepquant:
             act = moe.moe_grouped_qgemm_gateup_silu(xq, w_gu, sp, off, K, bufs.get("act"),
                                                     wtype=wtype)
             aq = moe.moe_quantize_act(wtype, act, bufs.get("aq_buf"))
             bufs["aq_buf"] = aq.data
         else:
             act = moe.moe_grouped_gemm_gateup_silu(x, w_gu, sp, off, K, bufs.get("act"))
-        if record:
-            moe.moe_time_next_gemm(evs[2], evs[3])
-        if keepquant:
-            eo = moe.moe_grouped_qgemm_down(aq, w_d, sp, off, w, bufs.get("expert_out"),
-                                            wtype=wtype)
-        else:
-            eo = moe.moe_grouped_gemm_down(act, w_d, sp, off, w, bufs.get("expert_out"))
-        if record:
-            ev.append(evs)
+        if not fused:
+            if record:
+                moe.moe_time_next_gemm(evs[2], evs[3])
+            if keepquant:
+                eo = moe.moe_grouped_qgemm_down(aq, w_d, sp, off, w, bufs.get("expert_out"),
+                                                wtype=wtype)
+            else:
+                eo = moe.moe_grouped_gemm_down(act, w_d, sp, off, w, bufs.get("expert_out"))
+            if record:
+                ev.append(evs)
         bufs.update(act=act, expert_out=eo)
         sd = gl = None
         if w_gu_s is not None:
@@ -308,6 +324,43 @@ def main():
 
     gu_ms = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev]))
     dn_ms = float(np.mean([c.elapsed_time(d_) for _, _, c, d_ in ev]))
+
+    fused_res = None
+    if fused_ok:
+        # the same steps with the fused expert FFN: eager (the fused kernel
+        # timed by its own events), then captured and replayed
+        ev.clear()
+        for i in range(max(args.warmup, L)):
+            step(False, layers[i % L], fused=True)
+        pool_f = [[new_event() for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for i in range(args.steps):
+            step(pool_f[i], layers[i % L], fused=True)
+        torch.cuda.synchronize()
+        f_elapsed = time.perf_counter() - t2
+        f_us = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev])) * 1e3
+        fused_res = {"ms_per_step": f_elapsed / args.steps * 1e3,
+                     "tokens_per_s": T * args.steps / f_elapsed,
+                     "ffn_kernel_us": f_us,
+                     "status": moe.fused_ffn_status(ws_f)}
+        if not args.no_graph:
+            gf = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gf):
+                for i in range(L):
+                    step(False, layers[i], fused=True)
+            reps = max(1, args.steps // L)
+            for _ in range(2):
+                gf.replay()
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            for _ in range(reps):
+                gf.replay()
+            torch.cuda.synchronize()
+            gf_elapsed = time.perf_counter() - t3
+            fused_res["hipgraph_ms_per_step"] = gf_elapsed / (reps * L) * 1e3
+            fused_res["hipgraph_tokens_per_s"] = T * reps * L / gf_elapsed
+            fused_res["status"] = moe.fused_ffn_status(ws_f)
     offsets = bufs["offsets"].cpu().numpy()
     gu, dn, touched = algorithmic_work(cfg, offsets)
     # the keep-quant GEMMs run int8 MFMAs (5.0 POP/s dense)
@@ -359,6 +412,7 @@ def main():
             "gbs_frac_of_hbm_peak": gemm_bytes / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
         "hipgraph": graph,
+        "fused_ffn": fused_res,
         "weight_sets": L,
         "cpu_baseline": None,
     }

@@ -265,6 +265,37 @@ moe_status moe_combine_gate(const void* expert_out, moe_dtype eo_dt, int T, int 
                             moe_dtype sh_dt, const float* gate_logit, void* out,
                             moe_dtype out_dt, moe_stream_t stream);
 
+/* Workspace bytes of moe_fused_expert_ffn: int32 counters for T tokens, E
+ * experts, top-K, grouped (sorted_pairs set) or not; 0 for T <= 0. */
+size_t moe_fused_expert_ffn_workspace_bytes(int T, int E, int K, int grouped);
+
+/* Decode expert FFN in one launch (gate-up -> SiLU -> down, [Issue 3094] N1,
+ * N2, N3): the same results as moe_grouped_gemm_gateup_silu followed by
+ * moe_grouped_gemm_down on the same arguments (act written as by the first,
+ * expert_out as by the second; the down k order may differ, so expert_out
+ * agrees to the GEMM tolerance, not bit for bit), with no launch boundary
+ * between the two: a row tile's down projection starts as soon as the act
+ * rows of that tile are complete, while other tiles' gate-up work is still
+ * running. Arguments as those two calls (packed w_gu and w_d, act [T*K, I]
+ * and expert_out [T*K, H] bf16, pair_w may be NULL). Meant for decode (a few
+ * rows per expert); it streams every tile, so with hundreds of rows per
+ * expert the two calls are faster. On MI355X at 32 tokens x 128 experts
+ * (H 2048, I 768) it takes about 198 us against 115 + 59 us for the two
+ * calls: its down phase has to take the gate-up's workgroup shape.
+ * ws: moe_fused_expert_ffn_workspace_bytes(T, E, K, sorted_pairs != NULL)
+ * bytes, 4-byte aligned, owned by the caller, zero-filled before its first
+ * use. Every launch leaves the counters zero again, so the same ws serves the
+ * next call on the same stream (calls that overlap on one ws race). Its last
+ * int32 is a status word: nonzero after a launch means one of the kernel's
+ * bounded waits gave up (it cannot happen when the hardware dispatches
+ * workgroups in order); expert_out is then invalid and ws must be zero-filled
+ * again. MOE_E_WORKSPACE for a short, NULL or misaligned ws. */
+moe_status moe_fused_expert_ffn(const uint16_t* x, int T, int H, const uint16_t* w_gu,
+                                const uint16_t* w_d, int E, int I, const int32_t* sorted_pairs,
+                                const int32_t* expert_offsets, int K, const float* pair_w,
+                                uint16_t* act, uint16_t* expert_out, void* ws, size_t ws_bytes,
+                                moe_stream_t stream);
+
 /*
  * Keep-quant grouped expert GEMMs ([PR 523] What changed: expert weights stay
  * in their GGUF block formats Q8_0 / Q4_K / Q5_K / Q6_K, activations are

@@ -27,6 +27,7 @@ __all__ = [
     "MoeError", "load", "lib_path", "moe_init", "PackedWeights", "moe_pack_weights",
     "moe_packed_weight_bytes", "Q8KBuffer", "QBuffer", "moe_q8k_bytes", "moe_quantize_q8k",
     "moe_q8_0_bytes", "moe_quantize_q8_0", "moe_quantize_act",
+    "moe_fused_expert_ffn_workspace_bytes", "moe_fused_expert_ffn", "fused_ffn_status",
     "moe_grouped_qgemm_gateup_silu", "moe_grouped_qgemm_down", "MOE_Q4_K", "MOE_Q5_K",
     "MOE_Q6_K", "MOE_Q8_0", "MOE_QTYPE", "KQ_BLOCK", "moe_router_logits", "moe_route",
     "moe_route_workspace_bytes", "moe_route_scored", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
@@ -51,6 +52,9 @@ SYMBOLS = {
     "moe_q8k_bytes": (ctypes.c_size_t, [_i, _i]),
     "moe_quantize_q8k": (_st, [_p, _i, _i, _p, _p]),
     "moe_q8_0_bytes": (ctypes.c_size_t, [_i, _i]),
+    "moe_fused_expert_ffn_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "moe_fused_expert_ffn": (_st, [_p, _i, _i, _p, _p, _i, _i, _p, _p, _i, _p, _p, _p, _p,
+                                   ctypes.c_size_t, _p]),
     "moe_quantize_q8_0": (_st, [_p, _i, _i, _p, _p]),
     "moe_grouped_qgemm_gateup_silu": (_st, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _i, _p, _p]),
     "moe_grouped_qgemm_down": (_st, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _p, _p, _p]),
@@ -467,6 +471,52 @@ def moe_grouped_qgemm_down(actq, w_d, sorted_pairs, expert_offsets, pair_w, expe
         _ptr(actq.data), P, I, _ptr(w_d), MOE_QTYPE[wtype], E, H, _ptr(sorted_pairs),
         _ptr(expert_offsets), _ptr(pair_w), _ptr(expert_out), _stream(stream)))
     return expert_out
+
+
+def moe_fused_expert_ffn_workspace_bytes(T, E, K, grouped=True):
+    return int(load().moe_fused_expert_ffn_workspace_bytes(T, E, K, int(bool(grouped))))
+
+
+def moe_fused_expert_ffn(x, w_gu, w_d, sorted_pairs, expert_offsets, K, pair_w, workspace,
+                         act=None, expert_out=None, stream=None):
+    """Gate-up, SiLU-mul and down in one launch (packed w_gu, w_d).
+    workspace: int32 tensor of moe_fused_expert_ffn_workspace_bytes bytes,
+    zero-filled before its first use (each launch leaves it zero)."""
+    import torch
+    _need(x, "x", torch.bfloat16, 2)
+    _need_packed(w_gu, "w_gu", "gateup")
+    _need_packed(w_d, "w_d", "plain")
+    T, H = x.shape
+    E, I = w_gu.E, w_gu.R // 2
+    if w_d.E != E or w_d.R != H or w_d.K != I or w_gu.K != H:
+        raise MoeError(3, f"w_gu {w_gu.E}x{w_gu.R}x{w_gu.K} and w_d {w_d.E}x{w_d.R}x{w_d.K} do not "
+                          f"match x [{T}, {H}]")
+    P = T * K
+    if sorted_pairs is not None:
+        _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(P,))
+    if expert_offsets is not None:
+        _need(expert_offsets, "expert_offsets", torch.int32, shape=(E + 1,))
+    if pair_w is not None:
+        _need(pair_w, "pair_w", torch.float32)
+        if pair_w.numel() != P:
+            raise MoeError(3, f"pair_w must hold {P} weights, got {pair_w.numel()}")
+    _need(workspace, "workspace", torch.int32)
+    if act is None:
+        act = torch.empty((P, I), dtype=torch.bfloat16, device=x.device)
+    if expert_out is None:
+        expert_out = torch.empty((P, H), dtype=torch.bfloat16, device=x.device)
+    _need(act, "act", torch.bfloat16, shape=(P, I))
+    _need(expert_out, "expert_out", torch.bfloat16, shape=(P, H))
+    _check(load().moe_fused_expert_ffn(
+        _ptr(x), T, H, _ptr(w_gu.data), _ptr(w_d.data), E, I, _ptr(sorted_pairs), _ptr(expert_offsets), K,
+        _ptr(pair_w), _ptr(act), _ptr(expert_out), _ptr(workspace),
+        workspace.numel() * 4, _stream(stream)))
+    return act, expert_out
+
+
+def fused_ffn_status(workspace):
+    """The status word of a fused-FFN workspace (0: every wait ended normally)."""
+    return int(workspace.view(-1)[-1].item())
 
 
 def moe_combine_gate(expert_out, T, K, topk_w=None, routed_scale=1.0, shared=None,

@@ -525,6 +525,56 @@ moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const uint16
                                          pair_w, expert_out, static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_fused_expert_ffn_workspace_bytes(int T, int E, int K, int grouped) {
+  if (T <= 0 || E < 1 || K < 1 || !fits_i32((long long)T * K)) return 0;
+  return (size_t)moe::fused_ffn_workspace_ints(T * K, E, grouped != 0) * 4;
+}
+
+moe_status moe_fused_expert_ffn(const uint16_t* x, int T, int H, const uint16_t* w_gu,
+                                const uint16_t* w_d, int E, int I, const int32_t* sorted_pairs,
+                                const int32_t* expert_offsets, int K, const float* pair_w,
+                                uint16_t* act, uint16_t* expert_out, void* ws, size_t ws_bytes,
+                                moe_stream_t stream) {
+  const char* fn = "moe_fused_expert_ffn";
+  DisarmTiming disarm;
+  clear_err();
+  if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
+  if (H <= 0 || H % 8) return fail(MOE_E_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);
+  if (I <= 0 || I % 8) return fail(MOE_E_SHAPE, "%s: I=%d must be a positive multiple of 8", fn, I);
+  if (E < 1 || E > kMaxE) return fail(MOE_E_SHAPE, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if (K < 1 || K > E || K > kMaxK)
+    return fail(MOE_E_SHAPE, "%s: K=%d outside [1, min(E=%d, %d)]", fn, K, E, kMaxK);
+  if ((sorted_pairs == nullptr) != (expert_offsets == nullptr))
+    return fail(MOE_E_INVALID, "%s: sorted_pairs and expert_offsets must both be set or both NULL",
+                fn);
+  if (sorted_pairs == nullptr && (E != 1 || K != 1))
+    return fail(MOE_E_INVALID, "%s: identity rows (NULL sorted_pairs) need E=1 and K=1, got E=%d K=%d",
+                fn, E, K);
+  if (!fits_i32((long long)T * K) || !fits_buf((long long)T * H) ||
+      !fits_buf((long long)T * K * I) || !fits_i32((long long)T * K * H) ||
+      !fits_packed(2 * I, H, true) || !fits_packed(H, I, false))
+    return fail(MOE_E_SHAPE, "%s: x or act exceeds 2^30 elements, T*K*H 2^31, or one expert's packed "
+                "weights 2^31 bytes", fn);
+  const int grouped = sorted_pairs != nullptr;
+  const size_t need = moe_fused_expert_ffn_workspace_bytes(T, E, K, grouped);
+  if (T > 0 && ws_bytes < need)
+    return fail(MOE_E_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, ws_bytes, need);
+  if (T == 0) return MOE_OK;
+  if (ws == nullptr || (uintptr_t)ws % 4 != 0)
+    return fail(MOE_E_WORKSPACE, "%s: ws is NULL or not 4-byte aligned (%zu bytes needed)", fn, need);
+  REQUIRE_PTR(fn, x);
+  REQUIRE_PTR(fn, w_gu);
+  REQUIRE_PTR(fn, w_d);
+  REQUIRE_PTR(fn, act);
+  REQUIRE_PTR(fn, expert_out);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_fused_ffn(x, T, H, w_gu, w_d, E, I, sorted_pairs,
+                                              expert_offsets, K, pair_w, act, expert_out,
+                                              static_cast<int*>(ws),
+                                              static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_combine_gate(const void* expert_out, moe_dtype eo_dt, int T, int K, int H,
                             const float* topk_w, float routed_scale, const void* shared,
                             moe_dtype sh_dt, const float* gate_logit, void* out,

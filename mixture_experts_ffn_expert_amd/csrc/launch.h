@@ -47,6 +47,15 @@ hipError_t timed_launch(const void* kernel, dim3 grid, dim3 block, void** args, 
 hipError_t launch_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
                          const float* bias, float* out, hipStream_t s);
 
+// gemm.hip: the decode expert FFN in one launch (gate-up, SiLU-mul, down);
+// ws holds fused_ffn_workspace_ints(P, E, grouped) int32 counters, zero
+// before the first launch and zero again after each one that reports no error
+int fused_ffn_workspace_ints(int P, int E, bool grouped);
+hipError_t launch_fused_ffn(const uint16_t* x, int T, int H, const uint16_t* w_gu,
+                            const uint16_t* w_d, int E, int I, const int32_t* sorted,
+                            const int32_t* offsets, int K, const float* pair_w, uint16_t* act,
+                            uint16_t* expert_out, int* ws, hipStream_t s);
+
 // combine.hip; dtype codes: 0 = f32, 1 = bf16
 hipError_t launch_combine(const void* eo, int eo_bf16, int T, int K, int H, const float* topk_w,
                           float routed_scale, const void* shared, int sh_bf16,

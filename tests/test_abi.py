@@ -237,3 +237,23 @@ def test_q8_0_buffer_and_refusals(lib):
     assert lib.moe_quantize_q8_0(A, 4, 40, A2, None) == 3 and "32" in _err(lib)
     assert lib.moe_quantize_q8_0(None, 0, 64, None, None) == 0
     assert lib.moe_quantize_q8_0(MIS, 4, 64, A2, None) == 1 and "aligned" in _err(lib)
+
+
+def test_fused_ffn_workspace_and_refusals(lib):
+    wb = lib.moe_fused_expert_ffn_workspace_bytes
+    assert wb(32, 128, 8, 1) == (2 * (16 + 128) + 1) * 4        # 16-row slots + one per expert
+    assert wb(40, 1, 1, 0) == (2 * 3 + 1) * 4                    # identity rows: 3 slots
+    assert wb(0, 8, 2, 1) == 0 and wb(4, 0, 1, 1) == 0
+    f = lib.moe_fused_expert_ffn
+    need = wb(4, 8, 2, 1)
+    #     x  T  H    w_gu w_d E  I   sorted offs K  pair_w act eo  ws  ws_bytes
+    assert f(A, 4, 256, A2, A2, 8, 64, A, A, 2, A, A, A, A, need - 4, None) == 4
+    assert "workspace" in _err(lib)
+    assert f(A, 4, 256, A2, A2, 8, 64, A, A, 2, A, A, A, None, need, None) == 4
+    assert f(A, 4, 256, A2, A2, 8, 64, A, A, 9, A, A, A, A, need, None) == 3 and "K=9" in _err(lib)
+    assert f(A, 4, 256, A2, A2, 8, 64, None, A, 2, A, A, A, A, need, None) == 1
+    assert f(A, 4, 250, A2, A2, 8, 64, A, A, 2, A, A, A, A, need, None) == 3
+    assert f(A, 4, 256, A2, A2, 2, 64, None, None, 2, A, A, A, A, need, None) == 1
+    assert f(A, 4, 256, MIS, A2, 8, 64, A, A, 2, A, A, A, A, need, None) == 1
+    assert "aligned" in _err(lib)
+    assert f(None, 0, 256, None, None, 8, 64, A, A, 2, None, None, None, None, 0, None) == 0
