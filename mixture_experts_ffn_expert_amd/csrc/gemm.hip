@@ -49,6 +49,7 @@
 
 #include "device_math.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -700,34 +701,6 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
 // ring slot a direct-to-LDS load writes and would otherwise wait for every
 // load in flight before each barrier.
 // ---------------------------------------------------------------------------
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ i32x4_t raw_rsrc(const void* base, uint32_t bytes) {
-  const unsigned long long b = (unsigned long long)base;
-  i32x4_t r = {(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)bytes, 0x00020000};
-  return r;
-}
-
-__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
-  // M0 is an input operand: the compiler places the LDS address there itself
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
-               : "memory");
-}
-
-// Wait until at most N of this wave's vector loads are in flight and all its
-// LDS reads are done, then barrier. Memory-clobbering, so no LDS access
-// moves across it.
-template <int N>
-__device__ __forceinline__ void wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
-}
-
 template <int EPI, int BM, int BN, int WM, int WN, int GM = 0, int BK = 64>
 __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   constexpr int NS = 2;                        // ring slots
@@ -997,13 +970,14 @@ void set_gemm_timing(hipEvent_t start, hipEvent_t stop) {
   t_stop = stop;
 }
 
-hipError_t timed_launch(const void* kernel, dim3 grid, dim3 block, void** args, hipStream_t s) {
+hipError_t timed_launch(const void* kernel, dim3 grid, dim3 block, void** args, hipStream_t s,
+                        size_t shm) {
   if (t_start != nullptr && t_stop != nullptr) {
     const hipEvent_t a = t_start, b = t_stop;
     t_start = t_stop = nullptr;
-    return hipExtLaunchKernel(kernel, grid, block, args, 0, s, a, b, 0);
+    return hipExtLaunchKernel(kernel, grid, block, args, shm, s, a, b, 0);
   }
-  return hipLaunchKernel(kernel, grid, block, args, 0, s);
+  return hipLaunchKernel(kernel, grid, block, args, shm, s);
 }
 
 template <typename Kernel>

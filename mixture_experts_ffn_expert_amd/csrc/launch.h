@@ -43,7 +43,8 @@ hipError_t launch_down(const uint16_t* act, int P, int I, const uint16_t* w_d, i
 void set_gemm_timing(hipEvent_t start, hipEvent_t stop);
 // Launch through hipExtLaunchKernel with the armed events (then disarmed), or
 // plainly when none are armed.
-hipError_t timed_launch(const void* kernel, dim3 grid, dim3 block, void** args, hipStream_t s);
+hipError_t timed_launch(const void* kernel, dim3 grid, dim3 block, void** args, hipStream_t s,
+                        size_t shm = 0);
 hipError_t launch_logits(const uint16_t* x, int T, int H, const uint16_t* w, int N,
                          const float* bias, float* out, hipStream_t s);
 

@@ -86,6 +86,9 @@ def test_quantize_q8_0_bit_exact(gpu_lib, R, K):
 def _routing(T, E, K, seed, empty=()):
     g = np.random.Generator(np.random.PCG64(seed))
     l = g.standard_normal((T, E)).astype(F32)
+    if empty == "skew":
+        l += (2.0 * np.log(1.0 / (1.0 + np.arange(E)))).astype(F32)
+        empty = ()
     for e in empty:
         l[:, e] = -50.0
     return O.route(l, K)
@@ -97,6 +100,11 @@ SHAPES = [
     (40, 768, 8, 3, 256, (2, 5)),        # 3 super-blocks, empty experts
     (24, 256, 6, 2, 264, ()),            # 1 super-block, column tail (I = 264)
     (200, 512, 4, 2, 768, ()),           # several 16-row tiles per expert
+    # at most 4 rows per expert on average (Q4_K: the lane-per-row kernel)
+    (16, 2048, 64, 4, 512, ()),          # 1 row per expert
+    (24, 768, 32, 4, 264, (3, 7)),       # 3 super-blocks, column tail, empty experts
+    (8, 256, 16, 2, 256, ()),            # 1 super-block
+    (48, 1024, 64, 5, 512, "skew"),      # skewed: some experts past 8 rows (two tiles)
 ]
 
 
@@ -128,8 +136,9 @@ def test_keepquant_gemms_stagewise(gpu_lib, T, H, E, K, I, empty, wtype):
 
 
 @pytest.mark.parametrize("wtype", FORMATS)
-def test_keepquant_identity_rows(gpu_lib, wtype):
-    T, H, I = 48, 512, 256
+@pytest.mark.parametrize("T", [48, 3])
+def test_keepquant_identity_rows(gpu_lib, wtype, T):
+    H, I = 512, 256
     g = np.random.Generator(np.random.PCG64(3))
     x = O.bf16_from_f32(g.standard_normal((T, H)).astype(F32))
     wgu = W.random_kq_blocks(wtype, g.integers(1 << 30), (1, 2 * I), H, 1 / math.sqrt(H))
