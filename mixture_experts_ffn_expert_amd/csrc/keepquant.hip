@@ -282,7 +282,7 @@ struct KqW<KQ_Q6_K> {
 template <>
 struct KqW<KQ_Q8_0> {
   uint2 q[8];
-  uint32_t d[8];
+  uint32_t d2;  // f16 scales of blocks 2 kc (low half) and 2 kc + 1 (high half)
 };
 
 // Loads the unit at byte offset `base` (kqOob-based offsets stay out of
@@ -319,8 +319,12 @@ __device__ __forceinline__ void kq_wload(KqW<FMT>& w, __amdgpu_buffer_rsrc_t r, 
     for (int b = 0; b < 8; ++b) {
       const uint32_t qo = base + 34 * b + 2 + kc * 8;
       w.q[b] = (b & 1) ? kq_load8(r, qo) : kq_load8_a2(r, qo);
-      w.d[b] = __builtin_amdgcn_raw_buffer_load_b16(r, base + 34 * b, 0, 0);
     }
+    // the four lanes of a row share its 8 scales: lane chunk kc loads two
+    // of them, the others come by lane exchange (kq_frag)
+    const uint32_t dl = __builtin_amdgcn_raw_buffer_load_b16(r, base + 68 * kc, 0, 0);
+    const uint32_t dh = __builtin_amdgcn_raw_buffer_load_b16(r, base + 68 * kc + 34, 0, 0);
+    w.d2 = (dl & 0xFFFFu) | (dh << 16);
   }
 }
 
@@ -481,11 +485,16 @@ __device__ __forceinline__ void kq_frag(float* acc, const KqW<FMT>& w, const KqA
       acc[i] = acc[i] + (dw * a.dx[i][0]) * (float)total;
     }
   } else {
+    // scales of blocks 2m, 2m + 1 from the lane of chunk m of this row
+    const int r16 = threadIdx.x & 15;
+    uint32_t dsc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dsc[m] = (uint32_t)__shfl((int)w.d2, r16 + 16 * m);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const i32x4v dot =
           __builtin_amdgcn_mfma_i32_16x16x32_i8(a.aop[b], kq_pair(w.q[b].x, w.q[b].y), z, 0, 0, 0);
-      const float dw = kq_f16(w.d[b]);
+      const float dw = kq_f16(dsc[b >> 1] >> (16 * (b & 1)));
       acc[0] = acc[0] + (dw * a.dx[0][b]) * (float)dot.x;
       acc[1] = acc[1] + (dw * a.dx[1][b]) * (float)dot.y;
       acc[2] = acc[2] + (dw * a.dx[2][b]) * (float)dot.z;
