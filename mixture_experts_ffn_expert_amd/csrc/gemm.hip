@@ -1029,19 +1029,17 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
         else
           return run(stream_kernel<EPI, 1, 1, 3, 4>, grid_for(g), 192, s, g);
       }
-      // tens of rows per tile: 32-row tiles; gate-up 64 columns (routed)
-      // or 32 (dense), down 32 columns, k split over 4 waves
+      // tens of rows per tile: 32-row tiles; gate-up 32 columns with k over
+      // 8 waves (routed) or 4 (dense), down 64 columns with k over 2 waves
+      // (measured at 16 rows per expert: 256 experts, 512 tokens, top-8)
       g.slots = slots_for(g.P, g.E, 32, grouped);
       if constexpr (EPI == EPI_GATEUP) {
-        if (grouped) {
-          g.nblk = (g.n_out + 63) / 64;
-          return run(stream_kernel<EPI, 2, 4, 4, 2>, grid_for(g), 256, s, g);
-        }
         g.nblk = (g.n_out + 31) / 32;
+        if (grouped) return run(stream_kernel<EPI, 2, 2, 8, 4>, grid_for(g), 512, s, g);
         return run(stream_kernel<EPI, 2, 2, 4, 4>, grid_for(g), 256, s, g);
       } else {
-        g.nblk = (g.n_out + 31) / 32;
-        return run(stream_kernel<EPI, 2, 2, 4, 2>, grid_for(g), 256, s, g);
+        g.nblk = (g.n_out + 63) / 64;
+        return run(stream_kernel<EPI, 2, 4, 2, 4>, grid_for(g), 128, s, g);
       }
     } else if constexpr (EPI == EPI_GATEUP) {
       // 256 x 256 tiles on 8 waves with the direct-to-LDS ring; blocks are
