@@ -8,7 +8,7 @@ activations; Q8_0 weights with Q8_0 activations).
   weight format match the oracle's exactly summed keep-quant dots within 2
   bf16 ulp (or 1e-2 rms near cancellation) per element and NMSE <= 1e-5 per
   tensor (the pages' bar is NMSE <= 5e-4), stage-wise (each stage fed the
-  oracle's input), over 1, 3 and 8 units of 256, ragged experts, empty
+  oracle's input), over 1, 3, 8 and 16 units of 256, ragged experts, empty
   experts, column tails and identity rows; and the four keep-quant decode
   workloads through the whole GPU chain.
 """
@@ -105,6 +105,7 @@ SHAPES = [
     (24, 768, 32, 4, 264, (3, 7)),       # 3 super-blocks, column tail, empty experts
     (8, 256, 16, 2, 256, ()),            # 1 super-block
     (48, 1024, 64, 5, 512, "skew"),      # skewed: some experts past 8 rows (two tiles)
+    (12, 4096, 8, 2, 1536, ()),          # 16 units per gate-up row, 6 per down row
 ]
 
 
