@@ -31,9 +31,10 @@
 //    with no LDS staging and no barrier in the k loop; the partial tiles meet
 //    once in LDS, added in a fixed order. The small work units keep every CU
 //    streaming to the end. HBM-bound by design.
-//  * tiled_dma_kernel (gate-up with hundreds of rows per expert): 256 x 256
+//  * tiled_dma_kernel (gate-up with hundreds of rows per expert): 320 x 256
 //    block tile on 8 waves, k step 64, a 2-stage LDS ring filled by
-//    direct-to-LDS buffer loads, XOR-swizzled rows, v_mfma_f32_32x32x16_bf16.
+//    direct-to-LDS buffer loads, XOR-swizzled rows, v_mfma_f32_32x32x16_bf16;
+//    the 32-row fragments past a tile's last row are skipped.
 //  * tiled_kernel (down with hundreds of rows per expert): 128 x 128 block
 //    tile, 4 waves of 64 x 64, k step 64 staged through LDS with padded rows
 //    (conflict-free 16-byte reads), register prefetch of the next k step
@@ -683,10 +684,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
 
 // ---------------------------------------------------------------------------
 // tiled_dma_kernel: BM x BN block tile (BN weight rows), WM x WN waves, k step
-// BK (64 or 32), two-slot LDS ring filled by direct-to-LDS buffer loads
+// BK (64 or 32), NS-slot LDS ring filled by direct-to-LDS buffer loads
 // (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at M0 + 16*l; an
-// out-of-range offset writes zeros). Stage s+1 is loading while stage s is
-// multiplied, with no register staging; the MFMA operands of the next 16-wide
+// out-of-range offset writes zeros). Stages s+1 .. s+NS-1 are loading while
+// stage s is multiplied, with no register staging (NS = 2 measured best: a
+// 4-slot ring of 32-wide stages ran 1-5 % slower); the MFMA operands of the next 16-wide
 // k step are read from LDS while the current step's MFMAs run, and the one
 // barrier per stage sits before the last k step of the stage, so the reads of
 // the next stage's first step overlap that step's MFMAs. A (activation rows):
@@ -696,14 +698,19 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void tiled_kernel(GemmArgs g) {
 // blocks as they come, where a fragment read of 16 rows is 256 contiguous
 // bytes.
 //
+// The 32-row fragments of a tile are dealt to the WM row waves in turn
+// (fragment i of wave wm holds rows (i*WM + wm)*32 ..), so a partial tile
+// (an expert's last) keeps its rows spread over the waves, and each wave
+// runs a copy of the k loop compiled for its count of fragments holding
+// rows: fragments wholly past the last row cost no LDS read and no MFMA.
+//
 // The loads are issued from inline assembly and the waits are explicit
 // (s_waitcnt vmcnt(N) lgkmcnt(0); s_barrier): the compiler cannot tell which
 // ring slot a direct-to-LDS load writes and would otherwise wait for every
 // load in flight before each barrier.
 // ---------------------------------------------------------------------------
-template <int EPI, int BM, int BN, int WM, int WN, int GM = 0, int BK = 64>
+template <int EPI, int BM, int BN, int WM, int WN, int GM = 0, int BK = 64, int NS = 2>
 __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
-  constexpr int NS = 2;                        // ring slots
   constexpr int NW = WM * WN;
   constexpr int NT = 64 * NW;
   constexpr int TM = BM / WM, TN = BN / WN;    // wave tile
@@ -716,6 +723,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   constexpr int OUT_COLS = (EPI == EPI_GATEUP) ? BN / 2 : BN;
   constexpr int CLD = OUT_COLS + 8;            // output staging row (elements)
   static_assert(BK == 64 || BK == 32, "k step");
+  static_assert(NS >= 2 && (NS - 2) * IPW <= 63, "ring depth (vmcnt range)");
   static_assert(IPW * RPL * NW == BM + BN, "loads per wave");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "swizzle period");
   static_assert(EPI != EPI_GATEUP || FN % 2 == 0, "gate-up pairs fragments");
@@ -833,7 +841,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   uint32_t aoff[FM][BK / 16], boff[FN][BK / 16];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int r = wm * TM + i * 32 + r32;
+    const int r = (i * WM + wm) * 32 + r32;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk)
       aoff[i][kk] = r * ROWB + (((kk * 2 + khalf) ^ ((r >> 1) & (CPR - 1))) * 16);
@@ -848,19 +856,23 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
       boff[f][kk] = BM * ROWB + (tb * KBS + kb) * 1024 + (c * 16 + rr) * 16;
     }
   }
-  // MFMA operands of one 16-wide k step, double-buffered across steps
+  // MFMA operands of one 16-wide k step, double-buffered across steps. Only
+  // the first NVA row fragments of the wave hold tile rows (NVA is a
+  // compile-time count, so every variant of the loop is straight-line code).
   constexpr int KK = BK / 16;
   bf16x8_t fa[2][FM], fb[2][FN];
-  auto read_step = [&](int buf, int slot, int kk) {
+  auto read_step = [&](auto nva_c, int buf, int slot, int kk) {
+    constexpr int NVA = decltype(nva_c)::value;
     const unsigned char* sb = ring + slot * STAGE;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(sb + aoff[i][kk]);
+    for (int i = 0; i < NVA; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(sb + aoff[i][kk]);
 #pragma unroll
     for (int f = 0; f < FN; ++f) fb[buf][f] = *reinterpret_cast<const bf16x8_t*>(sb + boff[f][kk]);
   };
-  auto mfma_step = [&](int buf) {
+  auto mfma_step = [&](auto nva_c, int buf) {
+    constexpr int NVA = decltype(nva_c)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < NVA; ++i)
 #pragma unroll
       for (int f = 0; f < FN; ++f)
         acc[i][f] =
@@ -868,35 +880,60 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   };
 
   const int nk = (g.kdim + BK - 1) / BK;
-  __syncthreads();  // row tables written; ring free
-  issue(0, 0);
-  wait_barrier<0>();  // stage 0 landed (every wave's loads)
-  if (nk > 1) issue(1, BK);
-  read_step(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
+  // The ring holds stages kt .. kt+NS-1 while stage kt is multiplied. Every
+  // wave issues IPW loads per stage, also for stages past the end of k (they
+  // read nothing and write zeros into a free slot), so that "stage kt+1 has
+  // landed" is always vmcnt((NS - 2) * IPW).
+  auto main_loop = [&](auto nva_c) {
+    constexpr int NVA = decltype(nva_c)::value;
+    __syncthreads();  // row tables written; ring free
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int b = kk & 1;
-      if (kk + 1 < KK) {
-        read_step(b ^ 1, cur, kk + 1);
-      } else if (kt + 1 < nk) {
-        // Stage kt+1 has landed (this wave's loads: vmcnt(0); the others':
-        // the barrier), and every wave has finished its LDS reads of stage
-        // kt (lgkmcnt(0) before the barrier), so its slot takes stage kt+2.
-        wait_barrier<0>();
-        if (kt + 2 < nk) issue(cur, (kt + 2) * BK);
-        read_step(b ^ 1, cur ^ 1, 0);
-      }
-      mfma_step(b);
-      // schedule: each MFMA followed by one LDS read of the next step, so
-      // the reads hide behind the MFMAs instead of bunching before them
+    for (int st = 0; st < NS; ++st) issue(st, st * BK);
+    wait_barrier<(NS - 1) * IPW>();  // stage 0 landed (every wave's loads)
+    if (NVA > 0) read_step(nva_c, 0, 0, 0);
+    int cur = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
 #pragma unroll
-      for (int q = 0; q < FM * FN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      for (int kk = 0; kk < KK; ++kk) {
+        const int b = kk & 1;
+        if (kk + 1 < KK) {
+          if (NVA > 0) read_step(nva_c, b ^ 1, cur, kk + 1);
+        } else if (kt + 1 < nk) {
+          // Stage kt+1 has landed (this wave's loads: the vmcnt; the others':
+          // the barrier), and every wave has finished its LDS reads of stage
+          // kt (lgkmcnt(0) before the barrier), so its slot takes stage
+          // kt+NS.
+          wait_barrier<(NS - 2) * IPW>();
+          issue(cur, (kt + NS) * BK);
+          if (NVA > 0) read_step(nva_c, b ^ 1, nxt, 0);
+        }
+        if (NVA > 0) {
+          mfma_step(nva_c, b);
+          // schedule: each MFMA followed by one LDS read of the next step,
+          // so the reads hide behind the MFMAs instead of bunching before
+          // them
+#pragma unroll
+          for (int q = 0; q < NVA * FN; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            if (q < NVA + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          }
+        }
       }
+      cur = nxt;
     }
+  };
+  // row fragment i of wave wm covers tile rows (i * WM + wm) * 32 + [0, 32)
+  const int frags = (rows + 31) / 32;
+  const int nva = min(FM, max(0, (frags - wm + WM - 1) / WM));
+  static_assert(FM <= 5, "main loop variants");
+  switch (nva) {
+    case 0: main_loop(std::integral_constant<int, 0>{}); break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (FM >= 2) main_loop(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (FM >= 3) main_loop(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr (FM >= 4) main_loop(std::integral_constant<int, 4>{}); break;
+    default: if constexpr (FM >= 5) main_loop(std::integral_constant<int, FM>{}); break;
   }
   wait_barrier<0>();  // ring free for the output staging
 
@@ -907,7 +944,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rr = wm * TM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+      const int rr = (i * WM + wm) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
       uint16_t* crow = smem + rr * CLD;
       if (EPI == EPI_GATEUP) {
 #pragma unroll
@@ -1042,10 +1079,13 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
         return run(stream_kernel<EPI, 2, 4, 2, 4>, grid_for(g), 128, s, g);
       }
     } else if constexpr (EPI == EPI_GATEUP) {
-      // 256 x 256 tiles on 8 waves with the direct-to-LDS ring; blocks are
+      // 320 x 256 tiles on 8 waves with the direct-to-LDS ring; blocks are
       // numbered expert by expert in groups of 4 row tiles, so a weight tile
-      // is reused by 4 consecutive workgroups while it is in L2
-      constexpr int BM = 256, BN = 256;
+      // is reused by 4 consecutive workgroups while it is in L2. 320 rows
+      // take a whole expert of the 4096-token prefill shape (205-301 rows)
+      // in one tile instead of 1-2 tiles of 256 (416 -> 352 us); the row
+      // fragments past a tile's last row are skipped
+      constexpr int BM = 320, BN = 256;
       g.nblk = (g.n_out + BN / 2 - 1) / (BN / 2);
       g.slots = slots_for(g.P, g.E, BM, grouped);
       return run(tiled_dma_kernel<EPI, BM, BN, 2, 4, 4>, grid_for(g), 512, s, g);

@@ -275,3 +275,28 @@ def test_timed_gemm_launch_matches_untimed(gpu_lib):
     t_gu = evs[0].elapsed_time(evs[1])
     t_dn = evs[2].elapsed_time(evs[3])
     assert 0.0 < t_gu < 100.0 and 0.0 < t_dn < 100.0, (t_gu, t_dn)
+
+
+def test_tiled_gateup_tail_tiles_bit_exact(gpu_lib):
+    """Every kind of partial row tile of the LDS-tiled gate-up: experts whose
+    last tile holds 1, 31, 32, 33, 63, 64, 65, 96, 129, 160, 200, 255, 288,
+    319 or 320 rows (tiles of 320 rows, 32-row fragments dealt to two row
+    waves, the fragments past the last row skipped), one empty expert, and
+    several full tiles per expert; exact arithmetic, so bit for bit."""
+    tails = [1, 31, 32, 33, 63, 64, 65, 96, 129, 160, 200, 255, 288, 319, 320, 0]
+    E, K, H, I = len(tails), 4, 264, 1000
+    counts = np.array([(3 if t else 0) * 320 + t for t in tails], dtype=np.int64)
+    counts[0] += (-int(counts.sum())) % K  # whole tokens
+    P = int(counts.sum())
+    T = P // K
+    print(f"tiled gate-up tail tiles T={T} H={H} E={E} K={K} I={I}", flush=True)
+    g = np.random.Generator(np.random.PCG64(4242))
+    ids = g.permutation(np.repeat(np.arange(E), counts)).reshape(T, K).astype(np.int32)
+    off, sp = O.group_pairs(ids, E)
+    assert np.array_equal(np.diff(off), counts)
+    x = _exact_bf16(91, (T, H), -4, 4, 1.0)
+    wgu = _exact_bf16(92, (E, 2 * I, H), -4, 4, 2.0 ** -6)
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), packed_gu(wgu), to_dev(sp),
+                                               to_dev(off), K)
+    torch.cuda.synchronize()
+    assert_bits_equal(bits(act), O.gateup_silu(x, wgu, sp, off, K), "act")
