@@ -15,7 +15,8 @@
 // so each of its K expert rows, its shared row and its output are single
 // 16-byte accesses (bf16) and a wavefront covers 1 KiB of each row: fully
 // coalesced. The sequential k order and the per-element arithmetic are
-// unchanged by the vector width.
+// unchanged by the vector width. A thread issues the loads of up to 8 of its
+// rows before the first add, so 8 loads per thread are in flight.
 #include "device_math.h"
 #include "launch.h"
 
@@ -80,16 +81,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const EO* __restrict__ eo,
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;  // +0
-  for (int k = 0; k < K; ++k) {
-    float v[8];
-    Vec8<EO>::load(eo + ((size_t)t * K + k) * H + h0, v);
-    if (w != nullptr) {
-      const float wk = w[(size_t)t * K + k];
+  // The K rows are loaded KB at a time, all KB loads issued before the first
+  // add (a row index past K - 1 re-reads row K - 1 and is not added), then
+  // summed in k order.
+  constexpr int KB = 8;
+  const EO* row = eo + (size_t)t * K * H + h0;
+  for (int k0 = 0; k0 < K; k0 += KB) {
+    float v[KB][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = wk * v[i];
+    for (int j = 0; j < KB; ++j) Vec8<EO>::load(row + (size_t)min(k0 + j, K - 1) * H, v[j]);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (k0 + j >= K) break;
+      if (w != nullptr) {
+        const float wk = w[(size_t)t * K + k0 + j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[j][i] = wk * v[j][i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + v[j][i];
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = acc[i] + v[i];
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = acc[i] * scale;
