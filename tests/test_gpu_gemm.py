@@ -215,7 +215,8 @@ def test_gemms_skewed_full_size_sampled(gpu_lib):
 
 @pytest.mark.parametrize("T,H,N,bias", [(16, 64, 8, False), (32, 2048, 128, False),
                                         (512, 2048, 1, False), (1000, 4096, 128, True),
-                                        (8192, 4096, 128, True)])
+                                        (1030, 520, 40, True), (4096, 2048, 128, False),
+                                        (8192, 4096, 128, True), (8200, 520, 40, False)])
 def test_router_logits_within_f32_bound(gpu_lib, T, H, N, bias):
     x = W.random_bf16(T + 1, (T, H))
     w = W.random_bf16(N + 2, (N, H), 1.0 / np.sqrt(H))
