@@ -117,6 +117,47 @@ def measured_traffic(workload):
     return int(m_val.group(1))
 
 
+def measure_ceilings(moe, torch, dev, reps=5):
+    """The chip's own ceilings, from the library's two micro-kernels: a
+    streaming read of a 2 GiB buffer (8x the last-level cache) and a
+    register-only bf16 MFMA loop on random operands. Each is timed by the
+    events its kernel records, mean of `reps` launches after two warm-ups."""
+    stream = torch.cuda.current_stream()
+
+    def timed(launch):
+        for _ in range(2):
+            launch()
+        evs = []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            for x in e:
+                x.record(stream)
+            evs.append(e)
+        torch.cuda.synchronize()
+        for a, b in evs:
+            moe.moe_time_next_gemm(a, b)
+            launch()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3  # s
+
+    nbytes = 1 << 31
+    buf = torch.full((nbytes,), 1, dtype=torch.uint8, device=dev)
+    out_i = torch.empty((moe.moe_probe_out_values(),), dtype=torch.int32, device=dev)
+    t_read = timed(lambda: moe.moe_probe_hbm_read(buf, out_i))
+    del buf
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    ops = torch.randn((1 << 21,), generator=gen, device=dev).to(torch.bfloat16)
+    out_f = torch.empty((moe.moe_probe_out_values(),), dtype=torch.float32, device=dev)
+    iters = 2000
+    t_mfma = timed(lambda: moe.moe_probe_mfma_bf16(ops, iters, out_f))
+    return {"hbm_read_gbs": nbytes / t_read / 1e9,
+            "mfma_bf16_tflops": moe.moe_probe_mfma_flops(iters) / t_mfma / 1e12,
+            "method": "library micro-kernels (moe_probe_hbm_read on a 2 GiB buffer; "
+                      "moe_probe_mfma_bf16, register-only v_mfma_f32_32x32x16_bf16 on random bf16 "
+                      f"operands, {iters} iterations), kernel-recorded events, mean of {reps}"}
+
+
 def cpu_baseline(d, sample_tokens):
     """The oracle (as it stands) on the first `sample_tokens` tokens."""
     import oracle
@@ -150,6 +191,8 @@ def main():
                          "step finds its weights in the 256 MB last-level cache (default 2)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the hipGraph-replay timing of the same steps")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the HBM-read and MFMA ceiling micro-kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM byte-counter calibration)")
     args = ap.parse_args()
@@ -322,8 +365,10 @@ def main():
         graph = {"steps": reps * L, "ms_per_step": g_elapsed / (reps * L) * 1e3,
                  "tokens_per_s": T * reps * L / g_elapsed}
 
-    gu_ms = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev]))
-    dn_ms = float(np.mean([c.elapsed_time(d_) for _, _, c, d_ in ev]))
+    gu_list = [a.elapsed_time(b) for a, b, _, _ in ev]
+    dn_list = [c.elapsed_time(d_) for _, _, c, d_ in ev]
+    gu_ms = float(np.mean(gu_list))
+    dn_ms = float(np.mean(dn_list))
 
     fused_res = None
     if fused_ok:
@@ -363,6 +408,7 @@ def main():
             fused_res["status"] = moe.fused_ffn_status(ws_f)
     offsets = bufs["offsets"].cpu().numpy()
     gu, dn, touched = algorithmic_work(cfg, offsets)
+    ceilings = None if args.no_ceilings else measure_ceilings(moe, torch, dev)
     # the keep-quant GEMMs run int8 MFMAs (5.0 POP/s dense)
     mfma_peak = MFMA_I8_PEAK_TOPS if keepquant else MFMA_BF16_PEAK_TFLOPS
     hbm_bound = (gu["flops"] / gu["bytes"]) < (mfma_peak * 1e12) / (HBM_PEAK_GBS * 1e9)
@@ -376,6 +422,13 @@ def main():
                 "unit": "TOP/s" if keepquant else "TFLOP/s", "frac": achieved / mfma_peak,
                 "traffic": None}
     roof["traffic"] = measured_traffic(args.workload)
+    if ceilings is not None:
+        # the same achieved figure against the chip's measured ceiling (the
+        # keep-quant kernels' int8 MFMAs have no measured ceiling here)
+        if hbm_bound:
+            roof["frac_of_measured"] = achieved / ceilings["hbm_read_gbs"]
+        elif not keepquant:
+            roof["frac_of_measured"] = achieved / ceilings["mfma_bf16_tflops"]
     roof["kernel"] = (f"grouped keep-quant gate-up GEMM + SiLU-mul ({wtype.upper()})" if keepquant
                       else "grouped gate-up GEMM + SiLU-mul")
     roof["algorithmic"] = {"bytes_per_launch": gu["bytes"], "flops_per_launch": gu["flops"],
@@ -406,6 +459,10 @@ def main():
         "roofline": roof,
         "grouped_gemm": {
             "gateup_us": gu_ms * 1e3, "down_us": dn_ms * 1e3,
+            "gateup_us_median": float(np.median(gu_list)) * 1e3,
+            "gateup_us_min": float(np.min(gu_list)) * 1e3,
+            "down_us_median": float(np.median(dn_list)) * 1e3,
+            "down_us_min": float(np.min(dn_list)) * 1e3,
             "tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12,
             "tflops_frac_of_mfma_peak": gemm_flops / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "algorithmic_gbs": gemm_bytes / (gemm_ms * 1e-3) / 1e9,
@@ -414,6 +471,7 @@ def main():
         "hipgraph": graph,
         "fused_ffn": fused_res,
         "weight_sets": L,
+        "measured_ceilings": ceilings,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

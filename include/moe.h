@@ -86,7 +86,8 @@ moe_status moe_init(void);
 
 /* Measurement only. Arms kernel timing for the next GEMM call
  * (moe_router_logits, moe_grouped_gemm_gateup_silu, moe_grouped_gemm_down,
- * moe_grouped_qgemm_gateup_silu or moe_grouped_qgemm_down)
+ * moe_grouped_qgemm_gateup_silu, moe_grouped_qgemm_down) or probe call
+ * (moe_probe_hbm_read, moe_probe_mfma_bf16)
  * made by this host thread: its kernel is launched so that it records its
  * own start and end into `start` and `stop` (hipEvent_t created by the
  * caller), and hipEventElapsedTime(start, stop) then gives the kernel's
@@ -94,6 +95,30 @@ moe_status moe_init(void);
  * not it launches (T = 0, a refused argument). Both NULL disarms; one NULL
  * is MOE_E_INVALID. Not for use under hipGraph capture. */
 moe_status moe_time_next_gemm(void* start, void* stop);
+
+/* Measurement only: the two ceilings the bench reads its figures against on
+ * the chip at hand, beside the datasheet peaks. Each launches 262,144
+ * threads (4,096 wavefronts) and writes one 32-bit value per thread to
+ * `out` (device memory of at least moe_probe_out_values() values; caller
+ * owned). A call armed by moe_time_next_gemm records its kernel's start and
+ * end like a GEMM call. Errors: NULL or misaligned pointers and sizes out of
+ * range give MOE_E_INVALID; launch failures MOE_E_HIP. */
+size_t moe_probe_out_values(void);
+
+/* Streaming read of `bytes` (a multiple of 16, at least 16) of the device
+ * buffer `buf` (16-byte aligned), 16-byte loads; out[i] (uint32) = XOR of
+ * every dword thread i read, so the XOR of all outputs is the XOR of every
+ * dword of the buffer. */
+moe_status moe_probe_hbm_read(const void* buf, size_t bytes, uint32_t* out, moe_stream_t stream);
+
+/* Register-only loop of v_mfma_f32_32x32x16_bf16: every wavefront runs `iters`
+ * (1 .. 2^20) iterations of 4 independent MFMAs (32,768 flops each) on bf16
+ * operands read from `ops` (n_ops 8-value operands = 16 * n_ops bytes,
+ * 16-byte aligned, 1 <= n_ops <= 2^26), i.e. moe_probe_mfma_flops(iters)
+ * flops per launch; out[i] (f32) = sum of thread i's accumulators. */
+moe_status moe_probe_mfma_bf16(const uint16_t* ops, size_t n_ops, int iters, float* out,
+                               moe_stream_t stream);
+double moe_probe_mfma_flops(int iters);
 
 typedef enum {
   MOE_PACK_PLAIN = 0,  /* a matrix [R, K] (down projection: R = H, K = I) */

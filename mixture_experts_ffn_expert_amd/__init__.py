@@ -31,7 +31,8 @@ __all__ = [
     "moe_grouped_qgemm_gateup_silu", "moe_grouped_qgemm_down", "MOE_Q4_K", "MOE_Q5_K",
     "MOE_Q6_K", "MOE_Q8_0", "MOE_QTYPE", "KQ_BLOCK", "moe_router_logits", "moe_route",
     "moe_route_workspace_bytes", "moe_route_scored", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
-    "moe_combine_gate", "moe_layer", "moe_time_next_gemm", "MOE_F32", "MOE_BF16", "MOE_F16", "SYMBOLS",
+    "moe_combine_gate", "moe_layer", "moe_time_next_gemm", "moe_probe_out_values",
+    "moe_probe_hbm_read", "moe_probe_mfma_bf16", "moe_probe_mfma_flops", "MOE_F32", "MOE_BF16", "MOE_F16", "SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +69,10 @@ SYMBOLS = {
     "moe_grouped_gemm_gateup_silu": (_st, [_p, _i, _i, _p, _i, _i, _p, _p, _i, _p, _p]),
     "moe_grouped_gemm_down": (_st, [_p, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p]),
     "moe_combine_gate": (_st, [_p, _i, _i, _i, _i, _p, ctypes.c_float, _p, _i, _p, _p, _i, _p]),
+    "moe_probe_out_values": (ctypes.c_size_t, []),
+    "moe_probe_hbm_read": (_st, [_p, ctypes.c_size_t, _p, _p]),
+    "moe_probe_mfma_bf16": (_st, [_p, ctypes.c_size_t, _i, _p, _p]),
+    "moe_probe_mfma_flops": (ctypes.c_double, [_i]),
 }
 
 
@@ -161,6 +166,43 @@ def moe_time_next_gemm(start=None, stop=None):
                               f"not exist yet")
         return ctypes.c_void_p(h)
     _check(load().moe_time_next_gemm(handle(start, "start"), handle(stop, "stop")))
+
+
+def moe_probe_out_values():
+    return int(load().moe_probe_out_values())
+
+
+def moe_probe_hbm_read(buf, out=None, stream=None):
+    """Measurement only: streaming read of the uint8 device buffer ``buf``
+    (its size a multiple of 16). Returns the per-thread XORs (int32 view of
+    the uint32 values; their XOR is the XOR of every dword of ``buf``)."""
+    import torch
+    _need(buf, "buf", torch.uint8, 1)
+    if out is None:
+        out = torch.empty((moe_probe_out_values(),), dtype=torch.int32, device=buf.device)
+    _need(out, "out", torch.int32, shape=(moe_probe_out_values(),))
+    _check(load().moe_probe_hbm_read(_ptr(buf), buf.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_probe_mfma_bf16(ops, iters, out=None, stream=None):
+    """Measurement only: register-only bf16 MFMA loop on operands from
+    ``ops`` (bf16, a multiple of 8 values); moe_probe_mfma_flops(iters)
+    flops per launch. Returns the per-thread accumulator sums (f32)."""
+    import torch
+    _need(ops, "ops", torch.bfloat16, 1)
+    if ops.numel() % 8:
+        raise MoeError(1, "ops must hold a multiple of 8 values")
+    if out is None:
+        out = torch.empty((moe_probe_out_values(),), dtype=torch.float32, device=ops.device)
+    _need(out, "out", torch.float32, shape=(moe_probe_out_values(),))
+    _check(load().moe_probe_mfma_bf16(_ptr(ops), ops.numel() // 8, int(iters), _ptr(out),
+                                      _stream(stream)))
+    return out
+
+
+def moe_probe_mfma_flops(iters):
+    return float(load().moe_probe_mfma_flops(int(iters)))
 
 
 def moe_router_logits(x, w, bias=None, out=None, stream=None):

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["route.hip", "gemm.hip", "combine.hip", "pack.hip", "keepquant.hip", "api.cpp"]
+SOURCES = ["route.hip", "gemm.hip", "combine.hip", "pack.hip", "keepquant.hip", "probe.hip",
+           "api.cpp"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -132,6 +132,44 @@ moe_status moe_time_next_gemm(void* start, void* stop) {
   return MOE_OK;
 }
 
+size_t moe_probe_out_values(void) { return (size_t)moe::kProbeBlocks * moe::kProbeThreads; }
+
+double moe_probe_mfma_flops(int iters) {
+  if (iters < 1) return 0.0;
+  const double waves = (double)moe::kProbeBlocks * moe::kProbeThreads / 64.0;
+  return waves * (double)iters * moe::kProbeMfmaChains * 32.0 * 32.0 * 16.0 * 2.0;
+}
+
+moe_status moe_probe_hbm_read(const void* buf, size_t bytes, uint32_t* out, moe_stream_t stream) {
+  const char* fn = "moe_probe_hbm_read";
+  DisarmTiming disarm;
+  clear_err();
+  REQUIRE_PTR(fn, buf);
+  REQUIRE_PTR(fn, out);
+  if (bytes < 16 || bytes % 16)
+    return fail(MOE_E_INVALID, "%s: bytes=%zu must be a positive multiple of 16", fn, bytes);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_probe_read(buf, bytes, out, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_probe_mfma_bf16(const uint16_t* ops, size_t n_ops, int iters, float* out,
+                               moe_stream_t stream) {
+  const char* fn = "moe_probe_mfma_bf16";
+  DisarmTiming disarm;
+  clear_err();
+  REQUIRE_PTR(fn, ops);
+  REQUIRE_PTR(fn, out);
+  if (n_ops < 1 || n_ops > (1u << 26))
+    return fail(MOE_E_INVALID, "%s: n_ops=%zu must be in [1, 2^26]", fn, n_ops);
+  if (iters < 1 || iters > (1 << 20))
+    return fail(MOE_E_INVALID, "%s: iters=%d must be in [1, 2^20]", fn, iters);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_probe_mfma(ops, (uint32_t)n_ops, iters, out,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_packed_weight_bytes(int E, int R, int K, moe_pack_kind kind) {
   if (E < 1 || R < 1 || K < 1 || K % 8 || (kind != MOE_PACK_PLAIN && kind != MOE_PACK_GATEUP))
     return 0;

@@ -58,6 +58,15 @@ hipError_t launch_fused_ffn(const uint16_t* x, int T, int H, const uint16_t* w_g
                             uint16_t* expert_out, int* ws, hipStream_t s);
 
 // combine.hip; dtype codes: 0 = f32, 1 = bf16
+// measurement micro-kernels (probe.hip): kProbeBlocks x kProbeThreads threads,
+// one 32-bit output per thread
+constexpr int kProbeBlocks = 1024;
+constexpr int kProbeThreads = 256;
+constexpr int kProbeMfmaChains = 4;  // MFMAs per wave and loop iteration
+hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t s);
+hipError_t launch_probe_mfma(const uint16_t* ops, uint32_t n_ops, int iters, float* out,
+                             hipStream_t s);
+
 hipError_t launch_combine(const void* eo, int eo_bf16, int T, int K, int H, const float* topk_w,
                           float routed_scale, const void* shared, int sh_bf16,
                           const float* gate_logit, void* out, int out_bf16, hipStream_t s);

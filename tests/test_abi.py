@@ -257,3 +257,24 @@ def test_fused_ffn_workspace_and_refusals(lib):
     assert f(A, 4, 256, MIS, A2, 8, 64, A, A, 2, A, A, A, A, need, None) == 1
     assert "aligned" in _err(lib)
     assert f(None, 0, 256, None, None, 8, 64, A, A, 2, None, None, None, None, 0, None) == 0
+
+
+def test_probe_sizes_and_refusals(lib):
+    # 1,024 workgroups of 256 threads; 4 chains of 32x32x16 MFMAs per wave
+    assert lib.moe_probe_out_values() == 262144
+    assert lib.moe_probe_mfma_flops(10) == 4096 * 10 * 4 * 32 * 32 * 16 * 2
+    assert lib.moe_probe_mfma_flops(0) == 0.0
+    assert lib.moe_probe_hbm_read(None, 1024, A, None) == 1 and "buf" in _err(lib)
+    assert lib.moe_probe_hbm_read(MIS, 1024, A, None) == 1 and "aligned" in _err(lib)
+    assert lib.moe_probe_hbm_read(A, 1000, A2, None) == 1 and "multiple of 16" in _err(lib)
+    assert lib.moe_probe_hbm_read(A, 0, A2, None) == 1
+    assert lib.moe_probe_mfma_bf16(A, 0, 10, A2, None) == 1 and "n_ops" in _err(lib)
+    assert lib.moe_probe_mfma_bf16(A, 64, 0, A2, None) == 1 and "iters" in _err(lib)
+    assert lib.moe_probe_mfma_bf16(A, 64, 1 << 21, A2, None) == 1
+    assert lib.moe_probe_mfma_bf16(A, 64, 10, None, None) == 1 and "out" in _err(lib)
+
+
+def test_refused_probe_call_disarms_timing(lib):
+    assert lib.moe_time_next_gemm(A, A2) == 0
+    assert lib.moe_probe_hbm_read(A, 8, A2, None) == 1
+    assert lib.moe_router_logits(None, 0, 16, None, 8, None, None, None) == 0

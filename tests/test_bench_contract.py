@@ -75,3 +75,8 @@ def test_default_run_prints_the_contract_line():
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-9
     assert 0 < roof["frac"] < 1
     assert d["cpu_baseline"] is None
+    # the chip's own ceilings from the library's micro-kernels, and the same
+    # achieved figure against the measured read ceiling
+    c = d["measured_ceilings"]
+    assert 1000 < c["hbm_read_gbs"] < 8000 and 100 < c["mfma_bf16_tflops"] < 2600
+    assert abs(roof["frac_of_measured"] - roof["achieved"] / c["hbm_read_gbs"]) < 1e-9
