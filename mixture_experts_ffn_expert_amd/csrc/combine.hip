@@ -27,8 +27,10 @@ struct Vec8;
 
 template <>
 struct Vec8<uint16_t> {  // bf16
+  template <bool NT = false>
   static __device__ __forceinline__ void load(const uint16_t* p, float v[8]) {
-    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+    const u32x4_t u = NT ? __builtin_nontemporal_load(q) : *q;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = __uint_as_float(u[i] << 16);
@@ -45,9 +47,11 @@ struct Vec8<uint16_t> {  // bf16
 
 template <>
 struct Vec8<float> {
+  template <bool NT = false>
   static __device__ __forceinline__ void load(const float* p, float v[8]) {
-    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
-    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+    const f32x4_t* q = reinterpret_cast<const f32x4_t*>(p);
+    const f32x4_t a = NT ? __builtin_nontemporal_load(q) : q[0];
+    const f32x4_t b = NT ? __builtin_nontemporal_load(q + 1) : q[1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[i] = a[i];
@@ -66,7 +70,7 @@ struct Vec8<float> {
   }
 };
 
-template <typename EO, typename SH, typename OUT>
+template <typename EO, typename SH, typename OUT, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const EO* __restrict__ eo, int K, int H,
                                                       const float* __restrict__ w, float scale,
                                                       const SH* __restrict__ sh,
@@ -89,7 +93,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const EO* __restrict__ eo,
   for (int k0 = 0; k0 < K; k0 += KB) {
     float v[KB][8];
 #pragma unroll
-    for (int j = 0; j < KB; ++j) Vec8<EO>::load(row + (size_t)min(k0 + j, K - 1) * H, v[j]);
+    for (int j = 0; j < KB; ++j)
+      Vec8<EO>::template load<NT>(row + (size_t)min(k0 + j, K - 1) * H, v[j]);
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
       if (k0 + j >= K) break;
@@ -123,9 +128,18 @@ static void launch3(const void* eo, int T, int K, int H, const float* w, float s
                     const void* sh, const float* gl, void* out, hipStream_t s) {
   const long long n_vec = (long long)T * (H / 8);
   const long long blocks = (n_vec + 255) / 256;
-  hipLaunchKernelGGL((combine_kernel<EO, SH, OUT>), dim3((unsigned)blocks), dim3(256), 0, s,
-                     static_cast<const EO*>(eo), K, H, w, scale, static_cast<const SH*>(sh), gl,
-                     static_cast<OUT*>(out), n_vec);
+  // expert_out larger than the 256 MiB last-level cache cannot still be
+  // there from the down projection that wrote it: its rows are read with the
+  // non-temporal hint (8192 tokens x 8 x 4096: 128 -> 111 us); a smaller one
+  // is read through the caches
+  if ((size_t)T * K * H * sizeof(EO) > ((size_t)256 << 20))
+    hipLaunchKernelGGL((combine_kernel<EO, SH, OUT, true>), dim3((unsigned)blocks), dim3(256), 0,
+                       s, static_cast<const EO*>(eo), K, H, w, scale, static_cast<const SH*>(sh),
+                       gl, static_cast<OUT*>(out), n_vec);
+  else
+    hipLaunchKernelGGL((combine_kernel<EO, SH, OUT, false>), dim3((unsigned)blocks), dim3(256), 0,
+                       s, static_cast<const EO*>(eo), K, H, w, scale, static_cast<const SH*>(sh),
+                       gl, static_cast<OUT*>(out), n_vec);
 }
 
 template <typename EO, typename SH>

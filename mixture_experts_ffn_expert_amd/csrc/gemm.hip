@@ -244,6 +244,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ bf16x8_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+// NT: the same load with the non-temporal hint (cache policy nt), for data
+// read once per launch: the weights of a grouped expert whose rows fit one
+// row tile of a streaming kernel. Decode gate-up 114.5 -> 103.0 us, down
+// 58.8 -> 53.1 us. Weights that several row tiles read (a dense expert's, a
+// busy expert's, the router's, and the tile kernels', whose workgroups share
+// weight tiles through the caches) measured slower with it: cached loads.
+template <bool NT>
+__device__ __forceinline__ bf16x8_t wload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(bf16x8_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? 2 : 0));
+}
 
 // ---------------------------------------------------------------------------
 // Packed expert weights (written once by moe_pack_weights, pack.hip). One
@@ -302,9 +313,52 @@ constexpr int stream_red_floats() {
   return KS * MF * ((EPI == EPI_GATEUP) ? 2 * NFO : NFO) * 4 * 64;
 }
 
+// The k loop of one wave of stream_body over [kb, ke): U 32-wide k steps of
+// loads in flight, then their MFMAs; the weight loads non-temporal if NTL.
+template <bool NTL, int MF, int NB, int U, typename BSoff>
+__device__ __forceinline__ void stream_kloop(f32x4_t (&acc)[MF][NB], __amdgpu_buffer_rsrc_t ra_rsrc,
+                                             __amdgpu_buffer_rsrc_t rb_rsrc,
+                                             const uint32_t (&va)[MF], const uint32_t (&vb)[NB],
+                                             BSoff bsoff, int kb, int ke, int kc) {
+  int k0 = kb;
+  for (; k0 + 32 * U <= ke; k0 += 32 * U) {
+    bf16x8_t a[U][MF], b[U][NB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t soff = (uint32_t)(k0 + u * 32) * 2u;
+      const uint32_t sb = bsoff(k0 + u * 32);
+#pragma unroll
+      for (int f = 0; f < NB; ++f) b[u][f] = wload8<NTL>(rb_rsrc, vb[f], sb);
+#pragma unroll
+      for (int i = 0; i < MF; ++i) a[u][i] = bload8(ra_rsrc, va[i], soff);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int f = 0; f < NB; ++f)
+          acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][f], acc[i][f], 0, 0, 0);
+  }
+  for (; k0 < ke; k0 += 32) {  // tail: 8-element chunks at or past ke read as zero
+    const bool in = k0 + kc < ke;
+    const uint32_t soff = (uint32_t)k0 * 2u;
+    bf16x8_t a[MF], b[NB];
+#pragma unroll
+    for (int f = 0; f < NB; ++f) b[f] = wload8<NTL>(rb_rsrc, in ? vb[f] : kOob, bsoff(k0));
+#pragma unroll
+    for (int i = 0; i < MF; ++i) a[i] = bload8(ra_rsrc, in ? va[i] : kOob, soff);
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int f = 0; f < NB; ++f)
+        acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
+  }
+}
+
 // red: LDS of stream_red_floats<EPI, MF, NFO, KS>() floats for the partial
 // tiles of the k waves.
-template <int EPI, int MF, int NFO, int KS, int U, bool COH = false>
+template <int EPI, int MF, int NFO, int KS, int U, bool COH = false, bool NT = false>
 __device__ __forceinline__ bool stream_body(const GemmArgs& g, int blk, float* red) {
   constexpr int NB = (EPI == EPI_GATEUP) ? 2 * NFO : NFO;  // B fragments per wave
   constexpr int BM = 16 * MF;
@@ -362,39 +416,61 @@ __device__ __forceinline__ bool stream_body(const GemmArgs& g, int blk, float* r
   const int kper = ((ksteps + KS - 1) / KS) * 32;
   const int kb = min(g.kdim, __builtin_amdgcn_readfirstlane(wave) * kper);
   const int ke = min(g.kdim, kb + kper);
-  int k0 = kb;
-  for (; k0 + 32 * U <= ke; k0 += 32 * U) {
-    bf16x8_t a[U][MF], b[U][NB];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t soff = (uint32_t)(k0 + u * 32) * 2u;
-      const uint32_t sb = bsoff(k0 + u * 32);
-#pragma unroll
-      for (int f = 0; f < NB; ++f) b[u][f] = bload8(rb_rsrc, vb[f], sb);
-#pragma unroll
-      for (int i = 0; i < MF; ++i) a[u][i] = bload8(ra_rsrc, va[i], soff);
+  // NT: the weight loads of a tile that is its expert's only one go out
+  // non-temporal (no other workgroup reads those weights); an expert with
+  // several row tiles has its weights re-read by each, through the caches.
+  if constexpr (NT) {
+    // the tile is its expert's only one when it starts at the expert's first
+    // row and ends at its last (uniform over the workgroup); a dense expert
+    // (no offsets: identity rows) is read by every row tile
+    bool once = false;
+    if (g.offsets != nullptr) {
+      const int o0 = __builtin_amdgcn_readfirstlane(g.offsets[e]);
+      const int o1 = __builtin_amdgcn_readfirstlane(g.offsets[e + 1]);
+      once = row0 == o0 && row0 + rows == o1;
     }
+    if (once)
+      stream_kloop<true, MF, NB, U>(acc, ra_rsrc, rb_rsrc, va, vb, bsoff, kb, ke, kc);
+    else
+      stream_kloop<false, MF, NB, U>(acc, ra_rsrc, rb_rsrc, va, vb, bsoff, kb, ke, kc);
+  } else {
+    // (written out here rather than through stream_kloop: the router-logit
+    // shapes keep 16 fewer VGPRs this way)
+    int k0 = kb;
+    for (; k0 + 32 * U <= ke; k0 += 32 * U) {
+      bf16x8_t a[U][MF], b[U][NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        const uint32_t soff = (uint32_t)(k0 + u * 32) * 2u;
+        const uint32_t sb = bsoff(k0 + u * 32);
+#pragma unroll
+        for (int f = 0; f < NB; ++f) b[u][f] = bload8(rb_rsrc, vb[f], sb);
+#pragma unroll
+        for (int i = 0; i < MF; ++i) a[u][i] = bload8(ra_rsrc, va[i], soff);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+          for (int f = 0; f < NB; ++f)
+            acc[i][f] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][f], acc[i][f], 0, 0, 0);
+    }
+    for (; k0 < ke; k0 += 32) {  // tail: 8-element chunks at or past ke read as zero
+      const bool in = k0 + kc < ke;
+      const uint32_t soff = (uint32_t)k0 * 2u;
+      bf16x8_t a[MF], b[NB];
+#pragma unroll
+      for (int f = 0; f < NB; ++f) b[f] = bload8(rb_rsrc, in ? vb[f] : kOob, bsoff(k0));
+#pragma unroll
+      for (int i = 0; i < MF; ++i) a[i] = bload8(ra_rsrc, in ? va[i] : kOob, soff);
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
         for (int f = 0; f < NB; ++f)
-          acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][f], acc[i][f], 0, 0, 0);
-  }
-  for (; k0 < ke; k0 += 32) {  // tail: 8-element chunks at or past ke read as zero
-    const bool in = k0 + kc < ke;
-    const uint32_t soff = (uint32_t)k0 * 2u;
-    bf16x8_t a[MF], b[NB];
-#pragma unroll
-    for (int f = 0; f < NB; ++f) b[f] = bload8(rb_rsrc, in ? vb[f] : kOob, bsoff(k0));
-#pragma unroll
-    for (int i = 0; i < MF; ++i) a[i] = bload8(ra_rsrc, in ? va[i] : kOob, soff);
-#pragma unroll
-    for (int i = 0; i < MF; ++i)
-#pragma unroll
-      for (int f = 0; f < NB; ++f)
-        acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
+          acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
+    }
   }
 
 #pragma unroll
@@ -435,10 +511,10 @@ __device__ __forceinline__ bool stream_body(const GemmArgs& g, int blk, float* r
   return true;
 }
 
-template <int EPI, int MF, int NFO, int KS, int U>
+template <int EPI, int MF, int NFO, int KS, int U, bool NT = false>
 __global__ __launch_bounds__(64 * KS) void stream_kernel(GemmArgs g) {
   __shared__ float red[stream_red_floats<EPI, MF, NFO, KS>()];
-  stream_body<EPI, MF, NFO, KS, U>(g, blockIdx.x, red);
+  stream_body<EPI, MF, NFO, KS, U, false, NT>(g, blockIdx.x, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -1075,9 +1151,11 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
         g.slots = slots_for(g.P, g.E, 16, grouped);
         g.nblk = (g.n_out + 15) / 16;
         if constexpr (EPI == EPI_GATEUP)
-          return run(stream_kernel<EPI, 1, 1, 8, 4>, grid_for(g), 512, s, g);
+          return grouped ? run(stream_kernel<EPI, 1, 1, 8, 4, true>, grid_for(g), 512, s, g)
+                         : run(stream_kernel<EPI, 1, 1, 8, 4>, grid_for(g), 512, s, g);
         else
-          return run(stream_kernel<EPI, 1, 1, 3, 4>, grid_for(g), 192, s, g);
+          return grouped ? run(stream_kernel<EPI, 1, 1, 3, 4, true>, grid_for(g), 192, s, g)
+                         : run(stream_kernel<EPI, 1, 1, 3, 4>, grid_for(g), 192, s, g);
       }
       // tens of rows per tile: 32-row tiles; gate-up 32 columns with k over
       // 8 waves (routed) or 4 (dense), down 64 columns with k over 2 waves
@@ -1085,11 +1163,12 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
       g.slots = slots_for(g.P, g.E, 32, grouped);
       if constexpr (EPI == EPI_GATEUP) {
         g.nblk = (g.n_out + 31) / 32;
-        if (grouped) return run(stream_kernel<EPI, 2, 2, 8, 4>, grid_for(g), 512, s, g);
+        if (grouped) return run(stream_kernel<EPI, 2, 2, 8, 4, true>, grid_for(g), 512, s, g);
         return run(stream_kernel<EPI, 2, 2, 4, 4>, grid_for(g), 256, s, g);
       } else {
         g.nblk = (g.n_out + 63) / 64;
-        return run(stream_kernel<EPI, 2, 4, 2, 4>, grid_for(g), 128, s, g);
+        return grouped ? run(stream_kernel<EPI, 2, 4, 2, 4, true>, grid_for(g), 128, s, g)
+                       : run(stream_kernel<EPI, 2, 4, 2, 4>, grid_for(g), 128, s, g);
       }
     } else if constexpr (EPI == EPI_GATEUP) {
       // 320 x 256 tiles on 8 waves with the direct-to-LDS ring; blocks are
@@ -1197,7 +1276,7 @@ __global__ __launch_bounds__(64 * kFusedKS) void fused_ffn_kernel(FusedArgs fa) 
     // is done, device-wide, before the count moves. That makes the count a
     // release for these stores without an agent-scope release fence, whose
     // L2 write-back per workgroup measured 2.2x slower for the whole FFN.
-    if (!stream_body<EPI_GATEUP, 1, 1, kFusedKS, 4, true>(fa.gu, blk, red)) return;
+    if (!stream_body<EPI_GATEUP, 1, 1, kFusedKS, 4, true, true>(fa.gu, blk, red)) return;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0)
@@ -1235,7 +1314,7 @@ __global__ __launch_bounds__(64 * kFusedKS) void fused_ffn_kernel(FusedArgs fa) 
   __syncthreads();
   const int st = go;
   if (st == 0) return;
-  if (st == 1) stream_body<EPI_DOWN, 1, kFusedDnNFO, kFusedKS, 3>(fa.dn, blk, red);
+  if (st == 1) stream_body<EPI_DOWN, 1, kFusedDnNFO, kFusedKS, 3, false, true>(fa.dn, blk, red);
   __syncthreads();
   if (tid == 0) {
     // a count only (no data is published through it): relaxed; every down
