@@ -163,7 +163,7 @@ moe_status moe_router_logits(const uint16_t* x, int T, int H, const uint16_t* w,
                              const float* bias, float* out, moe_stream_t stream);
 
 /* Bytes of device workspace moe_route needs for (T, E, K): 0 up to 4096
- * routed pairs (T*K), else 4 bytes per (4096-pair segment, expert). The
+ * routed pairs (T*K), else 4 bytes per (1024-pair segment, expert). The
  * workspace is scratch owned by the caller, 4-byte aligned, and may be
  * reused across calls on one stream; its contents on entry do not matter. */
 size_t moe_route_workspace_bytes(int T, int E, int K);

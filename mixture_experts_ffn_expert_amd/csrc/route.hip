@@ -13,7 +13,7 @@
 //   k-th logit, computes e_k = exp(l_k - l_0), every lane forms the same
 //   sequential f32 sum, lane k divides.
 // Grouping (group_kernel for up to 4096 pairs, else the count / scan /
-//   scatter kernels over 4096-pair segments): (i) per-wave expert histograms
+//   scatter kernels over 1024-pair segments): (i) per-wave expert histograms
 //   in LDS, (ii) an exclusive scan over experts (and segments) gives every
 //   wave its first output position per expert, (iii) each wave walks its part
 //   in order, 64 pairs at a time, ranks equal experts inside the 64 by
@@ -315,9 +315,13 @@ __global__ __launch_bounds__(256) void topk_scored_kernel(const float* __restric
 }
 
 constexpr int kGroupWaves = 8;
-// Pairs per workgroup segment of the multi-workgroup grouping (and the
-// largest pair count the single-workgroup kernel handles).
+// The largest pair count the single-workgroup grouping kernel handles.
 constexpr int kGroupSeg = 4096;
+// Pairs per workgroup segment of the multi-workgroup grouping above that:
+// 1024 pairs keep each wave's in-order walk to two steps of 64 (4096-pair
+// segments measured 23 us for the 32768 pairs of the 4096-token prefill
+// shape, mostly in the scatter's serial walk).
+constexpr int kScatterSeg = 1024;
 
 // Stable in-order scatter of pairs [beg, end) by one workgroup. cur[w][e]
 // holds, on entry, wave w's first output position for expert e; wave w owns
@@ -426,12 +430,12 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_kernel(const int32_t* 
 }
 
 // Multi-workgroup grouping, step 1: expert counts of each segment of
-// kGroupSeg pairs -> cnt[b][e].
+// kScatterSeg pairs -> cnt[b][e].
 __global__ __launch_bounds__(kGroupWaves * 64) void group_count_kernel(
     const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ cnt) {
   __shared__ int cur[kGroupWaves][kMaxE];
-  const int beg = blockIdx.x * kGroupSeg;
-  const int end = min(P, beg + kGroupSeg);
+  const int beg = blockIdx.x * kScatterSeg;
+  const int end = min(P, beg + kScatterSeg);
   count_segment(ids, beg, end, E, cur);
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int n = 0;
@@ -451,9 +455,17 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(int32_t* __restrict__ 
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int e = tid;  // E <= 1024: one expert per thread
+  // segments are read 16 at a time, all 16 loads in flight before the sums
+  constexpr int SB = 16;
   int tot = 0;
   if (e < E)
-    for (int b = 0; b < nseg; ++b) tot += cnt[(size_t)b * E + e];
+    for (int b0 = 0; b0 < nseg; b0 += SB) {
+      int v[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) v[j] = (b0 + j < nseg) ? cnt[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) tot += v[j];
+    }
   int incl = tot;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
@@ -466,10 +478,15 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(int32_t* __restrict__ 
   for (int w = 0; w < wave; ++w) run += wave_tot[w];
   if (e < E) {
     offsets[e] = run;
-    for (int b = 0; b < nseg; ++b) {
-      const int n = cnt[(size_t)b * E + e];
-      cnt[(size_t)b * E + e] = run;
-      run += n;
+    for (int b0 = 0; b0 < nseg; b0 += SB) {
+      int v[SB];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) v[j] = (b0 + j < nseg) ? cnt[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        if (b0 + j < nseg) cnt[(size_t)(b0 + j) * E + e] = run;
+        run += v[j];
+      }
     }
   }
   if (tid == 0) offsets[E] = P;
@@ -480,8 +497,8 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_scatter_kernel(
     const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ base,
     int32_t* __restrict__ sorted) {
   __shared__ int cur[kGroupWaves][kMaxE];
-  const int beg = blockIdx.x * kGroupSeg;
-  const int end = min(P, beg + kGroupSeg);
+  const int beg = blockIdx.x * kScatterSeg;
+  const int end = min(P, beg + kScatterSeg);
   count_segment(ids, beg, end, E, cur);
   // wave w's cursor = segment base + counts of waves before w (in order)
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -500,7 +517,7 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_scatter_kernel(
 size_t route_workspace_bytes(int T, int E, int K) {
   const long long P = (long long)T * K;
   if (P <= kGroupSeg) return 0;
-  const long long nseg = (P + kGroupSeg - 1) / kGroupSeg;
+  const long long nseg = (P + kScatterSeg - 1) / kScatterSeg;
   return (size_t)(nseg * E * 4);
 }
 
@@ -511,7 +528,7 @@ static hipError_t launch_grouping(const int32_t* ids, int P, int E, int32_t* off
     hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupWaves * 64), 0, s, ids, P, E, offsets,
                        sorted);
   } else {
-    const int nseg = (P + kGroupSeg - 1) / kGroupSeg;
+    const int nseg = (P + kScatterSeg - 1) / kScatterSeg;
     int32_t* cnt = static_cast<int32_t*>(ws);
     hipLaunchKernelGGL(group_count_kernel, dim3(nseg), dim3(kGroupWaves * 64), 0, s, ids, P, E,
                        cnt);

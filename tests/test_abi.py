@@ -124,7 +124,7 @@ def test_zero_tokens_is_a_no_op(lib):
 
 
 def test_route_workspace_query(lib):
-    assert lib.moe_route_workspace_bytes(8192, 128, 8) == 16 * 128 * 4
+    assert lib.moe_route_workspace_bytes(8192, 128, 8) == 64 * 128 * 4  # 1024-pair segments
     assert lib.moe_route_workspace_bytes(512, 128, 8) == 0
     assert lib.moe_route(A, 1000, 8, 8, A, A, A, A, None, 0, None) == 4
     assert "workspace" in _err(lib)

@@ -61,9 +61,11 @@ def test_route_is_deterministic(gpu_lib):
         assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("T,E,K", [(513, 128, 8), (512, 128, 8), (3000, 1024, 32), (8192, 256, 8)])
+@pytest.mark.parametrize("T,E,K", [(513, 128, 8), (512, 128, 8), (3000, 1024, 32), (8192, 256, 8),
+                                   (4100, 128, 8), (640, 64, 7)])
 def test_route_multi_segment_grouping_with_dirty_workspace(gpu_lib, T, E, K):
-    """Pair counts around and far above one 4096-pair segment; the caller's
+    """Pair counts around the single-workgroup limit (4096 pairs) and far above
+    it (1024-pair segments, a partial last one); the caller's
     workspace starts full of garbage and the result must not depend on it."""
     g = np.random.Generator(np.random.PCG64(T + E + K))
     l = g.standard_normal((T, E)).astype(F32)
