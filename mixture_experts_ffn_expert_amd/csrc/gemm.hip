@@ -1235,7 +1235,7 @@ hipError_t launch_down(const uint16_t* act, int P, int I, const uint16_t* w_d, i
 // routing weight, with no launch boundary between them. The first g1
 // workgroups are the gate-up tiles of the streaming kernel (16 rows x 16
 // columns, k over 8 waves); the rest are down tiles over the same 16-row
-// slots (16 rows x 128 columns). A down tile needs the whole act rows of its
+// slots (16 rows x 64 columns). A down tile needs the whole act rows of its
 // slot, written by the slot's gu.nblk gate-up workgroups: each of those,
 // once its act stores are complete, adds 1 to ready[slot]; a down workgroup
 // polls ready[slot] (relaxed) until it is gu.nblk, then acquires at agent
@@ -1258,7 +1258,7 @@ struct FusedArgs {
 };
 
 constexpr int kFusedKS = 8;
-constexpr int kFusedDnNFO = 8;  // down tiles: 16 rows x 128 columns
+constexpr int kFusedDnNFO = 4;  // down tiles: 16 rows x 64 columns (of 32, 64, 128, 256: fastest)
 constexpr unsigned kFusedSpin = 1u << 16;
 constexpr int kFusedRed =
     stream_red_floats<EPI_GATEUP, 1, 1, kFusedKS>() > stream_red_floats<EPI_DOWN, 1, kFusedDnNFO, kFusedKS>()
