@@ -279,9 +279,23 @@ def main():
         nws = moe.moe_fused_expert_ffn_workspace_bytes(T, E, K, True) // 4
         ws_f = torch.zeros((nws,), dtype=torch.int32, device=dev)
 
+    # the shared expert does not depend on the routing: it runs on a second
+    # stream (default priority), forked from and joined back into the layer's
+    # stream, so its small launches overlap the routing and the routed GEMMs
+    side = torch.cuda.Stream(device=dev)
+
     def step(record, lw, fused=False):
         w_r, w_gu, w_d = lw["w_r"], lw["w_gu"], lw["w_d"]
         w_gu_s, w_d_s, w_g = lw.get("w_gu_s"), lw.get("w_d_s"), lw.get("w_g")
+        main = torch.cuda.current_stream()  # the capture stream under graph capture
+        sd = gl = None
+        if w_gu_s is not None:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                sa = moe.moe_grouped_gemm_gateup_silu(x, w_gu_s, None, None, 1, bufs.get("sd_act"))
+                sd = moe.moe_grouped_gemm_down(sa, w_d_s, None, None, None, bufs.get("sd"))
+                gl = moe.moe_router_logits(x, w_g.view(1, H), None, bufs.get("gl"))
+            bufs.update(sd_act=sa, sd=sd, gl=gl)
         logits = moe.moe_router_logits(x, w_r, bias, bufs.get("logits"))
         bufs["logits"] = logits
         if router is None:
@@ -324,12 +338,8 @@ def main():
             if record:
                 ev.append(evs)
         bufs.update(act=act, expert_out=eo)
-        sd = gl = None
         if w_gu_s is not None:
-            sa = moe.moe_grouped_gemm_gateup_silu(x, w_gu_s, None, None, 1, bufs.get("sd_act"))
-            sd = moe.moe_grouped_gemm_down(sa, w_d_s, None, None, None, bufs.get("sd"))
-            gl = moe.moe_router_logits(x, w_g.view(1, H), None, bufs.get("gl"))
-            bufs.update(sd_act=sa, sd=sd, gl=gl)
+            main.wait_stream(side)
         out = moe.moe_combine_gate(eo, T, K, None, routed_scale, sd, gl, bufs.get("out"))
         bufs["out"] = out
 

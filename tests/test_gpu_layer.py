@@ -178,3 +178,63 @@ def test_layer_deterministic_and_graph_replay(gpu_lib):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(bufs["out"].view(torch.int16), out.view(torch.int16)), f"replay {i}"
+
+
+@pytest.mark.parametrize("n", [1, 4, 6])
+def test_shared_expert_on_a_second_stream(gpu_lib, n):
+    """The benchmark's layer schedule: the shared expert (gate-up, down, gate
+    logit) on a second stream forked from the layer's stream, the routed path
+    on the layer's stream, joined before the combine; three steps in a row and
+    a graph replay of the same schedule, each bit-identical to the sequential
+    layer."""
+    d = cached_inputs(n)
+    cfg = d["cfg"]
+    print(f"two-stream layer cfg={n} T={cfg.T}", flush=True)
+    t = _dev_inputs(d)
+    ref = bits(_run(t, cfg.K)).copy()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)
+    b = {}
+    router = None if t["router"] is None else dict(t["router"])
+    scale = 1.0 if router is None else router.pop("routed_scale")
+
+    def step():
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            sa = moe.moe_grouped_gemm_gateup_silu(t["x"], t["w_gu_s"], None, None, 1, b.get("sa"))
+            sd = moe.moe_grouped_gemm_down(sa, t["w_d_s"], None, None, None, b.get("sd"))
+            gl = moe.moe_router_logits(t["x"], t["w_g"].view(1, -1), None, b.get("gl"))
+        b.update(sa=sa, sd=sd, gl=gl)
+        logits = moe.moe_router_logits(t["x"], t["w_r"], t["router_bias"], b.get("logits"))
+        if router is None:
+            ids, w, off, sp = moe.moe_route(logits, cfg.K, b.get("ids"), b.get("w"),
+                                            b.get("off"), b.get("sp"), b.get("ws"))
+        else:
+            ids, w, off, sp = moe.moe_route_scored(
+                logits, cfg.K, selection_bias=t["selection_bias"], **router, topk_ids=b.get("ids"),
+                topk_w=b.get("w"), expert_offsets=b.get("off"), sorted_pairs=b.get("sp"),
+                workspace=b.get("ws"))
+        act = moe.moe_grouped_gemm_gateup_silu(t["x"], t["w_gu"], sp, off, cfg.K, b.get("act"))
+        eo = moe.moe_grouped_gemm_down(act, t["w_d"], sp, off, w, b.get("eo"))
+        b.update(logits=logits, ids=ids, w=w, off=off, sp=sp, act=act, eo=eo)
+        main.wait_stream(side)
+        out = moe.moe_combine_gate(eo, cfg.T, cfg.K, None, scale, sd, gl, b.get("out"))
+        b["out"] = out
+        return out
+
+    nws = moe.moe_route_workspace_bytes(cfg.T, cfg.E, cfg.K)
+    b["ws"] = torch.empty((nws,), dtype=torch.uint8, device=DEV) if nws else None
+    for _ in range(3):
+        out = step()
+        torch.cuda.synchronize()
+        assert_bits_equal(bits(out), ref, "two-stream layer output")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        b["out"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(bits(b["out"]), ref, "two-stream layer output, graph replay")
