@@ -163,6 +163,85 @@ def measure_ceilings(moe, torch, dev, reps=5):
                       f"operands, {iters} iterations), kernel-recorded events, mean of {reps}"}
 
 
+EP_SHARDS = 8
+
+
+def expert_parallel_share(moe, torch, x, layers, off_dev, sp_dev, w_dev, cfg, reps=10):
+    """The grouped GEMMs that each GPU of an EP_SHARDS-way expert-parallel
+    layer would run, timed one owner at a time on this GPU. The owner of a
+    contiguous block of E / EP_SHARDS experts receives only its own pairs,
+    their x rows grouped by expert (what the all-to-all would deliver; the
+    gather is done here outside the timed region), and runs the same gate-up
+    and down calls on them with K = 1, identity pair order and offsets
+    rebased to its first pair, on its experts' packed weights only. The
+    exchange itself is not part of it. Weight sets rotate over the layers so
+    that every timed call reads its weights from HBM."""
+    E, K, H, I = cfg.E, cfg.K, cfg.H, cfg.I
+    dev = x.device
+    nb = E // EP_SHARDS
+    off = off_dev.cpu().numpy().astype(np.int64)
+    sp = sp_dev.cpu().numpy().astype(np.int64)
+    w_flat = w_dev.reshape(-1)
+    L = len(layers)
+    shards = []
+    for b in range(EP_SHARDS):
+        e0, e1 = b * nb, (b + 1) * nb
+        q0, q1 = int(off[e0]), int(off[e1])
+        n = q1 - q0
+        row = {"experts": [e0, e1], "pairs": n,
+               "touched_experts": int(np.count_nonzero(np.diff(off[e0:e1 + 1])))}
+        if n == 0:
+            row.update(gateup_us=0.0, down_us=0.0)
+            shards.append(row)
+            continue
+        pairs = torch.from_numpy(sp[q0:q1]).to(dev)
+        xs = x.index_select(0, pairs // K).contiguous()
+        offs = torch.from_numpy((off[e0:e1 + 1] - q0).astype(np.int32)).to(dev)
+        idn = torch.arange(n, dtype=torch.int32, device=dev)
+        ws = w_flat.index_select(0, pairs).contiguous()
+        act = torch.empty((n, I), dtype=torch.bfloat16, device=dev)
+        eo = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+        wsets = [(lw["w_gu"].experts(e0, e1), lw["w_d"].experts(e0, e1)) for lw in layers]
+
+        def call(i, evs=None):
+            wgu, wd = wsets[i % L]
+            if evs:
+                moe.moe_time_next_gemm(evs[0], evs[1])
+            moe.moe_grouped_gemm_gateup_silu(xs, wgu, idn, offs, 1, act)
+            if evs:
+                moe.moe_time_next_gemm(evs[2], evs[3])
+            moe.moe_grouped_gemm_down(act, wd, idn, offs, ws, eo)
+
+        for i in range(2 * L):
+            call(i)
+        pool = []
+        for _ in range(reps):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            for e in evs:
+                e.record()
+            pool.append(evs)
+        torch.cuda.synchronize()
+        for i in range(reps):
+            call(i, pool[i])
+        torch.cuda.synchronize()
+        gu = float(np.mean([a.elapsed_time(b_) for a, b_, _, _ in pool])) * 1e3
+        dn = float(np.mean([c.elapsed_time(d_) for _, _, c, d_ in pool])) * 1e3
+        row.update(gateup_us=gu, down_us=dn)
+        shards.append(row)
+    tot = [r["gateup_us"] + r["down_us"] for r in shards]
+    hot = int(np.argmax(tot))
+    flops_hot = 2.0 * shards[hot]["pairs"] * 3 * H * I
+    return {
+        "shards": EP_SHARDS, "experts_per_shard": nb, "per_shard": shards,
+        "max_gemm_us": max(tot), "mean_gemm_us": float(np.mean(tot)),
+        "imbalance": max(tot) / float(np.mean(tot)) if np.mean(tot) > 0 else None,
+        "slowest_shard": hot,
+        "slowest_shard_tflops": flops_hot / (tot[hot] * 1e-6) / 1e12 if tot[hot] > 0 else None,
+        "note": "GEMMs only, at each owner's real pair count; the two all-to-all "
+                "exchanges are not built (one GPU)",
+    }
+
+
 def cpu_baseline(d, sample_tokens):
     """The oracle (as it stands) on the first `sample_tokens` tokens."""
     import oracle
@@ -196,6 +275,8 @@ def main():
                          "step finds its weights in the 256 MB last-level cache (default 2)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the hipGraph-replay timing of the same steps")
+    ap.add_argument("--no-ep-share", action="store_true",
+                    help="skip timing the GEMMs at each expert-parallel owner's share")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the HBM-read and MFMA ceiling micro-kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -423,6 +504,10 @@ def main():
             fused_res["status"] = moe.fused_ffn_status(ws_f)
     offsets = bufs["offsets"].cpu().numpy()
     gu, dn, touched = algorithmic_work(cfg, offsets)
+    ep = None
+    if not keepquant and not args.no_ep_share and E % EP_SHARDS == 0:
+        ep = expert_parallel_share(moe, torch, x, layers, bufs["offsets"], bufs["sorted"],
+                                   bufs["w"], cfg)
     ceilings = None if args.no_ceilings else measure_ceilings(moe, torch, dev)
     # the keep-quant GEMMs run int8 MFMAs (5.0 POP/s dense)
     mfma_peak = MFMA_I8_PEAK_TOPS if keepquant else MFMA_BF16_PEAK_TFLOPS
@@ -485,6 +570,7 @@ def main():
         },
         "hipgraph": graph,
         "fused_ffn": fused_res,
+        "expert_parallel_share": ep,
         "weight_sets": L,
         "measured_ceilings": ceilings,
         "cpu_baseline": None,

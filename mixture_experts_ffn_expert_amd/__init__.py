@@ -312,6 +312,15 @@ class PackedWeights:
     def __repr__(self):
         return f"PackedWeights(E={self.E}, R={self.R}, K={self.K}, kind={self.kind!r})"
 
+    def experts(self, e0, e1):
+        """Experts [e0, e1) as PackedWeights viewing the same memory (each
+        expert's packed matrix is contiguous): the block of experts that one
+        rank owns when experts are split across GPUs."""
+        if not (0 <= e0 < e1 <= self.E):
+            raise MoeError(3, f"expert range [{e0}, {e1}) outside [0, {self.E})")
+        per = self.data.numel() // self.E
+        return PackedWeights(self.data[e0 * per:e1 * per], e1 - e0, self.R, self.K, self.kind)
+
 
 def moe_packed_weight_bytes(E, R, K, kind):
     return int(load().moe_packed_weight_bytes(E, R, K, MOE_PACK[kind]))

@@ -1139,11 +1139,15 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
     return run(stream_kernel<EPI, 2, 4, 4, 2>, grid_for(g), 256, s, g);
   } else {
     const double avg_rows = grouped ? (double)g.P / (double)g.E : (double)g.P;
-    // LDS tiles pay off with hundreds of rows per expert and enough tiles to
-    // occupy the chip; everything else streams the weights.
+    // LDS tiles pay off with hundreds of rows per expert, from a modest
+    // number of tiles on: at 16 experts with 4,000 to 9,000 pairs (one
+    // owner's share when 128 experts are split over 8 GPUs) they beat the
+    // streaming kernels from 128 nominal tiles on for gate-up (613 -> 308 us
+    // at 9,058 pairs of the skewed router) and from 256 on for down (60 ->
+    // 30 us at 4,032 prefill pairs); a 512-row dense expert still streams.
     const int tbm = (EPI == EPI_GATEUP) ? 256 : 128;
     const long long tiled_blocks = (long long)(g.P / tbm) * ((g.n_out + 127) / 128);
-    if (avg_rows <= 24.0 || tiled_blocks < 512) {
+    if (avg_rows <= 24.0 || tiled_blocks < (EPI == EPI_GATEUP ? 128 : 256)) {
       if (avg_rows <= 8.0) {
         // decode-like: 16-row tiles of 16 columns; gate-up (gate + up
         // fragments) splits k over 8 waves with 4 k steps in flight per

@@ -278,3 +278,24 @@ def test_refused_probe_call_disarms_timing(lib):
     assert lib.moe_time_next_gemm(A, A2) == 0
     assert lib.moe_probe_hbm_read(A, 8, A2, None) == 1
     assert lib.moe_router_logits(None, 0, 16, None, 8, None, None, None) == 0
+
+
+def test_packed_weights_expert_block_views(lib):
+    """PackedWeights.experts views the block of experts one expert-parallel
+    owner holds: the same bytes, one packed expert after another."""
+    import torch
+    E, R, K = 8, 2 * 96, 136
+    n = moe.moe_packed_weight_bytes(E, R, K, "gateup")
+    per = n // E
+    assert per * E == n and per % 1024 == 0
+    data = torch.arange(n, dtype=torch.int64).remainder(251).to(torch.uint8)
+    pw = moe.PackedWeights(data, E, R, K, "gateup")
+    blk = pw.experts(2, 5)
+    assert (blk.E, blk.R, blk.K, blk.kind) == (3, R, K, "gateup")
+    assert blk.data.numel() == moe.moe_packed_weight_bytes(3, R, K, "gateup")
+    assert blk.data.data_ptr() == data.data_ptr() + 2 * per
+    assert torch.equal(blk.data, data[2 * per:5 * per])
+    assert pw.experts(0, E).data.numel() == n
+    for e0, e1 in [(-1, 2), (3, 3), (5, 2), (0, E + 1)]:
+        with pytest.raises(moe.MoeError):
+            pw.experts(e0, e1)

@@ -80,3 +80,13 @@ def test_default_run_prints_the_contract_line():
     c = d["measured_ceilings"]
     assert 1000 < c["hbm_read_gbs"] < 8000 and 100 < c["mfma_bf16_tflops"] < 2600
     assert abs(roof["frac_of_measured"] - roof["achieved"] / c["hbm_read_gbs"]) < 1e-9
+    # the GEMMs at each expert-parallel owner's share: every pair belongs to
+    # exactly one owner, and the slowest owner bounds the layer
+    ep = d["expert_parallel_share"]
+    assert ep["shards"] == 8 and ep["experts_per_shard"] == 16
+    rows = ep["per_shard"]
+    assert sum(r["pairs"] for r in rows) == 32 * 8
+    assert [r["experts"] for r in rows] == [[16 * b, 16 * b + 16] for b in range(8)]
+    tot = [r["gateup_us"] + r["down_us"] for r in rows]
+    assert all(t > 0 for t, r in zip(tot, rows) if r["pairs"] > 0)
+    assert ep["max_gemm_us"] == max(tot)
