@@ -1142,12 +1142,13 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
     // LDS tiles pay off with hundreds of rows per expert, from a modest
     // number of tiles on: at 16 experts with 4,000 to 9,000 pairs (one
     // owner's share when 128 experts are split over 8 GPUs) they beat the
-    // streaming kernels from 128 nominal tiles on for gate-up (613 -> 308 us
-    // at 9,058 pairs of the skewed router) and from 256 on for down (60 ->
-    // 30 us at 4,032 prefill pairs); a 512-row dense expert still streams.
+    // streaming kernels from 32 nominal tiles on for gate-up (613 -> 308 us
+    // at 9,058 pairs of the skewed router, 88 -> 57 us at 4,032 prefill
+    // pairs) and from 256 on for down (60 -> 30 us at 4,032 prefill pairs);
+    // a 512-row dense expert still streams.
     const int tbm = (EPI == EPI_GATEUP) ? 256 : 128;
     const long long tiled_blocks = (long long)(g.P / tbm) * ((g.n_out + 127) / 128);
-    if (avg_rows <= 24.0 || tiled_blocks < (EPI == EPI_GATEUP ? 128 : 256)) {
+    if (avg_rows <= 24.0 || tiled_blocks < (EPI == EPI_GATEUP ? 32 : 256)) {
       if (avg_rows <= 8.0) {
         // decode-like: 16-row tiles of 16 columns; gate-up (gate + up
         // fragments) splits k over 8 waves with 4 k steps in flight per
@@ -1175,6 +1176,15 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
                        : run(stream_kernel<EPI, 2, 4, 2, 4>, grid_for(g), 128, s, g);
       }
     } else if constexpr (EPI == EPI_GATEUP) {
+      if ((long long)(g.P / 320) * ((g.n_out + 127) / 128) < 512) {
+        // too few 320-row tiles to fill 256 CUs: 128 x 128 tiles (64 act
+        // columns), 8 waves of 32 x 64, give 2.5x as many workgroups
+        // (prefill share of 16 experts: 88 -> 57 us)
+        constexpr int BM = 128, BN = 128;
+        g.nblk = (g.n_out + BN / 2 - 1) / (BN / 2);
+        g.slots = slots_for(g.P, g.E, BM, grouped);
+        return run(tiled_dma_kernel<EPI, BM, BN, 4, 2, 4>, grid_for(g), 512, s, g);
+      }
       // 320 x 256 tiles on 8 waves with the direct-to-LDS ring; blocks are
       // numbered expert by expert in groups of 4 row tiles, so a weight tile
       // is reused by 4 consecutive workgroups while it is in L2. 320 rows

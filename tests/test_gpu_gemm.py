@@ -86,9 +86,10 @@ def test_gemms_bit_exact_on_exact_arithmetic(gpu_lib, T, H, E, K, I, skew):
 
 @pytest.mark.parametrize("skew", [False, True])
 def test_tiled_gemms_bit_exact_on_exact_arithmetic(gpu_lib, skew):
-    """Large enough for the LDS-tiled kernels (256-row gate-up tiles with the
-    direct-to-LDS ring, 128-row down tiles): 16384 pairs over 16 experts, with
-    k tails (H = 520, I = 1000 are not multiples of 64) and a column tail."""
+    """Large enough for the LDS-tiled kernels (128-row gate-up tiles with the
+    direct-to-LDS ring at this size, 128-row down tiles): 16384 pairs over 16
+    experts, with k tails (H = 520, I = 1000 are not multiples of 64) and a
+    column tail."""
     T, H, E, K, I = 4096, 520, 16, 4, 1000
     print(f"exact tiled gemm T={T} H={H} E={E} K={K} I={I} skew={skew}", flush=True)
     seed = 77 + int(skew)
@@ -278,19 +279,29 @@ def test_timed_gemm_launch_matches_untimed(gpu_lib):
     assert 0.0 < t_gu < 100.0 and 0.0 < t_dn < 100.0, (t_gu, t_dn)
 
 
-def test_tiled_gateup_tail_tiles_bit_exact(gpu_lib):
-    """Every kind of partial row tile of the LDS-tiled gate-up: experts whose
-    last tile holds 1, 31, 32, 33, 63, 64, 65, 96, 129, 160, 200, 255, 288,
-    319 or 320 rows (tiles of 320 rows, 32-row fragments dealt to two row
-    waves, the fragments past the last row skipped), one empty expert, and
-    several full tiles per expert; exact arithmetic, so bit for bit."""
-    tails = [1, 31, 32, 33, 63, 64, 65, 96, 129, 160, 200, 255, 288, 319, 320, 0]
-    E, K, H, I = len(tails), 4, 264, 1000
-    counts = np.array([(3 if t else 0) * 320 + t for t in tails], dtype=np.int64)
+TAILS_320 = [1, 31, 32, 33, 63, 64, 65, 96, 129, 160, 200, 255, 288, 319, 320, 0]
+TAILS_128 = [1, 31, 32, 33, 63, 64, 65, 96, 127, 128, 0]
+
+
+@pytest.mark.parametrize("bm,tails,full,I", [(320, TAILS_320, 3, 2000), (128, TAILS_128, 2, 1000)],
+                         ids=["tiles320", "tiles128"])
+def test_tiled_gateup_tail_tiles_bit_exact(gpu_lib, bm, tails, full, I):
+    """Every kind of partial row tile of the LDS-tiled gate-up, in both of its
+    tile shapes: 320-row tiles (32-row fragments dealt to two row waves) once
+    there are at least 512 of them nominally (P / 320 times 128-column
+    blocks), else 128-row tiles (one fragment per row wave). Experts whose
+    last tile holds from 1 row to a full tile, one empty expert, and several
+    full tiles per expert; the fragments past a tile's last row are skipped.
+    Exact arithmetic, so bit for bit."""
+    E, K, H = len(tails), 4, 264
+    counts = np.array([(full if t else 0) * bm + t for t in tails], dtype=np.int64)
     counts[0] += (-int(counts.sum())) % K  # whole tokens
     P = int(counts.sum())
     T = P // K
-    print(f"tiled gate-up tail tiles T={T} H={H} E={E} K={K} I={I}", flush=True)
+    nominal = (P // 320) * ((I + 127) // 128)
+    assert (nominal >= 512) == (bm == 320), nominal
+    assert (P // 256) * ((I + 127) // 128) >= 32 and P / E > 24    # tiled, not streamed
+    print(f"tiled gate-up tail tiles bm={bm} T={T} H={H} E={E} K={K} I={I}", flush=True)
     g = np.random.Generator(np.random.PCG64(4242))
     ids = g.permutation(np.repeat(np.arange(E), counts)).reshape(T, K).astype(np.int32)
     off, sp = O.group_pairs(ids, E)
