@@ -275,8 +275,10 @@ def main():
                          "step finds its weights in the 256 MB last-level cache (default 2)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the hipGraph-replay timing of the same steps")
-    ap.add_argument("--no-ep-share", action="store_true",
-                    help="skip timing the GEMMs at each expert-parallel owner's share")
+    ap.add_argument("--ep-share", action="store_true",
+                    help="also time the GEMMs at each expert-parallel owner's share (the "
+                         "same kernels at other shapes: kept out of the default run so that "
+                         "a kernel trace of it averages the layer's launches only)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the HBM-read and MFMA ceiling micro-kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -505,7 +507,7 @@ def main():
     offsets = bufs["offsets"].cpu().numpy()
     gu, dn, touched = algorithmic_work(cfg, offsets)
     ep = None
-    if not keepquant and not args.no_ep_share and E % EP_SHARDS == 0:
+    if args.ep_share and not keepquant and E % EP_SHARDS == 0:
         ep = expert_parallel_share(moe, torch, x, layers, bufs["offsets"], bufs["sorted"],
                                    bufs["w"], cfg)
     ceilings = None if args.no_ceilings else measure_ceilings(moe, torch, dev)

@@ -55,7 +55,8 @@ def test_algorithmic_work_formulas():
 @pytest.mark.gpu
 def test_default_run_prints_the_contract_line():
     r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3",
-                        "--warmup", "1", "--no-cpu-baseline", "--no-graph", "--no-fused"],
+                        "--warmup", "1", "--no-cpu-baseline", "--no-graph", "--no-fused",
+                        "--ep-share"],
                        capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
