@@ -150,6 +150,12 @@ def measure_ceilings(moe, torch, dev, reps=5):
     out_i = torch.empty((moe.moe_probe_out_values(),), dtype=torch.int32, device=dev)
     t_read = timed(lambda: moe.moe_probe_hbm_read(buf, out_i))
     del buf
+    # negative control: the same read of a 64 MiB buffer, which the 256 MB
+    # last-level cache can hold between launches
+    small = 1 << 26
+    buf = torch.full((small,), 1, dtype=torch.uint8, device=dev)
+    t_small = timed(lambda: moe.moe_probe_hbm_read(buf, out_i))
+    del buf
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
     ops = torch.randn((1 << 21,), generator=gen, device=dev).to(torch.bfloat16)
@@ -157,10 +163,71 @@ def measure_ceilings(moe, torch, dev, reps=5):
     iters = 2000
     t_mfma = timed(lambda: moe.moe_probe_mfma_bf16(ops, iters, out_f))
     return {"hbm_read_gbs": nbytes / t_read / 1e9,
+            "control_64MiB_read_gbs": small / t_small / 1e9,
             "mfma_bf16_tflops": moe.moe_probe_mfma_flops(iters) / t_mfma / 1e12,
             "method": "library micro-kernels (moe_probe_hbm_read on a 2 GiB buffer; "
                       "moe_probe_mfma_bf16, register-only v_mfma_f32_32x32x16_bf16 on random bf16 "
                       f"operands, {iters} iterations), kernel-recorded events, mean of {reps}"}
+
+
+class GpuStateSampler:
+    """Clock, power and temperature of the GPU in use, read from its sysfs
+    node (found by PCI address) by a thread that samples them every 100 ms
+    while a region runs. Best effort: None where the node is not readable."""
+
+    def __init__(self, torch, dev):
+        import threading
+        p = torch.cuda.get_device_properties(dev)
+        self.base = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
+                     f"{p.pci_device_id:02x}.0")
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _cur_mhz(self, name):
+        import re
+        try:
+            for line in open(os.path.join(self.base, name)):
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                    return int(m.group(1)) if m else None
+        except OSError:
+            pass
+        return None
+
+    def _hwmon(self, name, scale):
+        import glob
+        for f in sorted(glob.glob(os.path.join(self.base, "hwmon", "hwmon*", name))):
+            try:
+                return int(open(f).read().strip()) / scale
+            except (OSError, ValueError):
+                continue
+        return None
+
+    def read(self):
+        return {"sclk_mhz": self._cur_mhz("pp_dpm_sclk"), "mclk_mhz": self._cur_mhz("pp_dpm_mclk"),
+                "power_w": self._hwmon("power1_average", 1e6) or self._hwmon("power1_input", 1e6),
+                "temp_c": self._hwmon("temp2_input", 1e3) or self._hwmon("temp1_input", 1e3)}
+
+    def _run(self):
+        while not self._stop.is_set():
+            self.samples.append(self.read())
+            self._stop.wait(0.1)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self, idle):
+        out = {"sysfs": self.base, "samples": len(self.samples), "idle_before": idle}
+        for k in ("sclk_mhz", "mclk_mhz", "power_w", "temp_c"):
+            v = [s[k] for s in self.samples if s[k] is not None]
+            out[k] = ({"min": min(v), "median": float(np.median(v)), "max": max(v)} if v else None)
+        return out
 
 
 EP_SHARDS = 8
@@ -435,12 +502,16 @@ def main():
     for i in range(max(args.warmup, L)):
         step(False, layers[i % L])
     pool = [[new_event() for _ in range(4)] for _ in range(args.steps)]
+    sampler = GpuStateSampler(torch, dev)
+    idle = sampler.read()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(pool[i] if i % TIMING_EVERY == 0 else False, layers[i % L])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with sampler:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(pool[i] if i % TIMING_EVERY == 0 else False, layers[i % L])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    gpu_state = sampler.summary(idle)
 
     graph = None
     if not args.no_graph:
@@ -575,6 +646,7 @@ def main():
         "expert_parallel_share": ep,
         "weight_sets": L,
         "measured_ceilings": ceilings,
+        "gpu_state": gpu_state,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

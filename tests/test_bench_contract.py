@@ -91,3 +91,8 @@ def test_default_run_prints_the_contract_line():
     tot = [r["gateup_us"] + r["down_us"] for r in rows]
     assert all(t > 0 for t, r in zip(tot, rows) if r["pairs"] > 0)
     assert ep["max_gemm_us"] == max(tot)
+    # GPU clock / power while the steps ran (sysfs of the device, best effort)
+    # and the cache-resident read that the 2 GiB read is compared against
+    gs = d["gpu_state"]
+    assert gs["samples"] >= 1 and gs["sysfs"].startswith("/sys/bus/pci/devices/")
+    assert c["control_64MiB_read_gbs"] > 0
