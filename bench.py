@@ -14,7 +14,12 @@ workload. The steps cycle through `--layers` weight sets (same values,
 distinct addresses), so no step finds its weights in the last-level cache
 left by the step before, as in a model whose consecutive MoE layers hold
 distinct weights. `hipgraph` times the same steps captured once into a HIP
-graph and replayed.
+graph and replayed. `measured_ceilings` holds the chip's read and MFMA
+ceilings from the library's micro-kernels (with a cache-resident read as a
+control) and `gpu_state` the clock, power and temperature sampled while the
+steps ran. With `--ep-share`, `expert_parallel_share` times the grouped
+GEMMs of each owner of E/8 experts on its own pairs (one GPU's share of an
+8-way expert-parallel layer).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
        (--workload picks one of the ten workloads, default 2: the 32-token
