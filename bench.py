@@ -177,8 +177,9 @@ def measure_ceilings(moe, torch, dev, reps=5):
 
 class GpuStateSampler:
     """Clock, power and temperature of the GPU in use, read from its sysfs
-    node (found by PCI address) by a thread that samples them every 100 ms
-    while a region runs. Best effort: None where the node is not readable."""
+    node (found by PCI address) by a thread that samples them 5 ms into a
+    region, then every 50 ms, and once at its end. Best effort: None where
+    the node is not readable."""
 
     def __init__(self, torch, dev):
         import threading
@@ -215,9 +216,10 @@ class GpuStateSampler:
                 "temp_c": self._hwmon("temp2_input", 1e3) or self._hwmon("temp1_input", 1e3)}
 
     def _run(self):
-        while not self._stop.is_set():
+        # the first sample 5 ms in, when the clock has had time to follow the
+        # load, then every 50 ms
+        while not self._stop.wait(0.005 if not self.samples else 0.05):
             self.samples.append(self.read())
-            self._stop.wait(0.1)
 
     def __enter__(self):
         self._thread.start()
@@ -226,6 +228,7 @@ class GpuStateSampler:
     def __exit__(self, *exc):
         self._stop.set()
         self._thread.join()
+        self.samples.append(self.read())  # at the end of the region
 
     def summary(self, idle):
         out = {"sysfs": self.base, "samples": len(self.samples), "idle_before": idle}
