@@ -180,3 +180,132 @@ def test_refusals():
         O.select_scored(s, 5, None, 4, 2)          # 2 groups of 2 hold only 4 experts
     with pytest.raises(ValueError):
         O.router_scores(s, "relu")
+
+
+# --- the butterfly order of the full-softmax sum and the bias rounding point ---
+def _vec(case):
+    z = np.zeros((1, case["E"]), F32)
+    for e, h in case["nonzero"].items():
+        z[0, int(e)] = F32(float.fromhex(h))
+    return z
+
+
+def _butterfly_reversed(z):
+    """Planted mistake: lane sums as in the reading, butterfly m = 1 .. 32."""
+    T, E = z.shape
+    p = np.zeros((T, 64), F32)
+    for e in range(E):
+        p[:, e % 64] = (p[:, e % 64] + z[:, e]).astype(F32)
+    for m in (1, 2, 4, 8, 16, 32):
+        p = (p + p[:, np.arange(64) ^ m]).astype(F32)
+    return p[:, 0]
+
+
+def _contiguous_chunks(z):
+    """Planted mistake: lane l sums the contiguous chunk [l*c, (l+1)*c)."""
+    T, E = z.shape
+    c = -(-E // 64)
+    p = np.zeros((T, 64), F32)
+    for lane in range(64):
+        for e in range(lane * c, min(E, (lane + 1) * c)):
+            p[:, lane] = (p[:, lane] + z[:, e]).astype(F32)
+    for m in (32, 16, 8, 4, 2, 1):
+        p = (p + p[:, np.arange(64) ^ m]).astype(F32)
+    return p[:, 0]
+
+
+def _sequential(z):
+    acc = np.zeros(z.shape[0], F32)
+    for e in range(z.shape[1]):
+        acc = (acc + z[:, e]).astype(F32)
+    return acc
+
+
+def _lane_decreasing(z):
+    """Planted mistake: each lane adds its elements in decreasing e."""
+    T, E = z.shape
+    p = np.zeros((T, 64), F32)
+    for e in reversed(range(E)):
+        p[:, e % 64] = (p[:, e % 64] + z[:, e]).astype(F32)
+    for m in (32, 16, 8, 4, 2, 1):
+        p = (p + p[:, np.arange(64) ^ m]).astype(F32)
+    return p[:, 0]
+
+
+_MUTANT_SUMS = {"reversed_butterfly": _butterfly_reversed, "contiguous_chunks": _contiguous_chunks,
+                "sequential": _sequential, "lane_decreasing_e": _lane_decreasing}
+
+
+@pytest.mark.parametrize("case", _cases()["sum_order_cases"], ids=lambda c: c["name"])
+def test_golden_butterfly_sum_order(case):
+    got = O.tree_sum64(_vec(case))
+    assert got.tolist() == [float.fromhex(case["expected_hex"])], (case["name"], got)
+
+
+@pytest.mark.parametrize("case", _cases()["sum_order_cases"], ids=lambda c: c["name"])
+def test_planted_sum_orders_fail_golden(case):
+    exp = float.fromhex(case["expected_hex"])
+    for name, h in case["mutants_hex"].items():
+        got = _MUTANT_SUMS[name](_vec(case))
+        assert got.tolist() == [float.fromhex(h)], name     # the fixture separates them
+        assert got[0] != exp, name
+
+
+def _softmax_logits(case):
+    l = np.full((1, case["E"]), F32(case["other_logit"]), F32)
+    for e, h in case["logits_hex"].items():
+        l[0, int(e)] = F32(float.fromhex(h))
+    return l
+
+
+@pytest.mark.parametrize("case", _cases()["softmax_sum_order_cases"], ids=lambda c: c["name"])
+def test_golden_softmax_denominator_order(case):
+    l = _softmax_logits(case)
+    s = O.router_scores(l, "softmax")
+    assert float(s[0, 0]) == float.fromhex(case["expected_s0_hex"])
+    # the route through the softmax router carries the same first weight
+    ids, w, _, _ = O.route_scored(l, 2, "softmax", None, 1, 1, "max", False)
+    assert ids[0, 0] == 0 and float(w[0, 0]) == float.fromhex(case["expected_s0_hex"])
+    # the fixture's premise: the two small terms are each under half an ulp of 1
+    z = O.pexp((l - l.max()).astype(F32))
+    assert 2.0 ** -25 < float(z[0, 1]) < 2.0 ** -24 and z[0, 1] == z[0, 3]
+
+
+@pytest.mark.parametrize("case", _cases()["softmax_sum_order_cases"], ids=lambda c: c["name"])
+def test_planted_softmax_sum_orders_fail_golden(case):
+    l = _softmax_logits(case)
+    z = O.pexp((l - l.max()).astype(F32))
+    exp = float.fromhex(case["expected_s0_hex"])
+    for S in (_sequential(z), np.sum(z, axis=1, dtype=F32), _butterfly_reversed(z),
+              _contiguous_chunks(z)):
+        s0 = float((z[0, 0] / S[0]).astype(F32))
+        assert s0 == float.fromhex(case["mutants_s0_hex"]["sequential_or_pairwise_sum"])
+        assert s0 != exp
+
+
+def _bias_inputs(case):
+    x = O.bf16_from_f32(np.array(case["x"], F32))
+    w = np.array([[float.fromhex(h) for h in row] for row in case["w_r_hex"]], F32)
+    wb = O.bf16_from_f32(w)
+    assert np.array_equal(O.f32_from_bf16(wb), w), "fixture not bf16-exact"
+    return x, wb, np.array(case["bias"], F32)
+
+
+@pytest.mark.parametrize("case", _cases()["logit_bias_cases"], ids=lambda c: c["name"])
+def test_golden_logit_bias_rounding(case):
+    x, wb, b = _bias_inputs(case)
+    got = O.router_logits(x, wb, b)
+    exp = np.array([[float.fromhex(h) for h in row] for row in case["expected_hex"]], F32)
+    assert np.array_equal(got, exp), got
+
+
+@pytest.mark.parametrize("case", _cases()["logit_bias_cases"], ids=lambda c: c["name"])
+def test_planted_float64_bias_add_fails_golden(case):
+    x, wb, b = _bias_inputs(case)
+    xf = O.f32_from_bf16(x).astype(np.float64)
+    wf = O.f32_from_bf16(wb).astype(np.float64)
+    bad = (xf @ wf.T + b.astype(np.float64)[None, :]).astype(F32)   # one rounding, after the bias
+    mut = np.array([[float.fromhex(h) for h in row]
+                    for row in case["mutants_hex"]["bias_added_in_float64"]], F32)
+    exp = np.array([[float.fromhex(h) for h in row] for row in case["expected_hex"]], F32)
+    assert np.array_equal(bad, mut) and not np.array_equal(bad, exp)
