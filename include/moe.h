@@ -86,12 +86,12 @@ moe_status moe_init(void);
 
 /* Measurement only. Arms kernel timing for the next GEMM call
  * (moe_router_logits, moe_grouped_gemm_gateup_silu, moe_grouped_gemm_down,
- * moe_grouped_qgemm_gateup_silu, moe_grouped_qgemm_down) or probe call
- * (moe_probe_hbm_read, moe_probe_mfma_bf16)
+ * moe_grouped_qgemm_gateup_silu, moe_grouped_qgemm_down), combine call
+ * (moe_combine_gate) or probe call (moe_probe_hbm_read, moe_probe_mfma_bf16)
  * made by this host thread: its kernel is launched so that it records its
  * own start and end into `start` and `stop` (hipEvent_t created by the
  * caller), and hipEventElapsedTime(start, stop) then gives the kernel's
- * duration without the launch gap. The next GEMM call disarms it whether or
+ * duration without the launch gap. The next such call disarms it whether or
  * not it launches (T = 0, a refused argument). Both NULL disarms; one NULL
  * is MOE_E_INVALID. Not for use under hipGraph capture. */
 moe_status moe_time_next_gemm(void* start, void* stop);

@@ -619,6 +619,7 @@ moe_status moe_combine_gate(const void* expert_out, moe_dtype eo_dt, int T, int 
                             moe_dtype out_dt, moe_stream_t stream) {
   const char* fn = "moe_combine_gate";
   clear_err();
+  DisarmTiming disarm;
   moe_status st = check_dtype(fn, "expert_out", eo_dt);
   if (st != MOE_OK) return st;
   if (shared != nullptr) {

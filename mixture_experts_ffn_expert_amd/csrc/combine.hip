@@ -132,14 +132,14 @@ static void launch3(const void* eo, int T, int K, int H, const float* w, float s
   // there from the down projection that wrote it: its rows are read with the
   // non-temporal hint (8192 tokens x 8 x 4096: 128 -> 111 us); a smaller one
   // is read through the caches
-  if ((size_t)T * K * H * sizeof(EO) > ((size_t)256 << 20))
-    hipLaunchKernelGGL((combine_kernel<EO, SH, OUT, true>), dim3((unsigned)blocks), dim3(256), 0,
-                       s, static_cast<const EO*>(eo), K, H, w, scale, static_cast<const SH*>(sh),
-                       gl, static_cast<OUT*>(out), n_vec);
-  else
-    hipLaunchKernelGGL((combine_kernel<EO, SH, OUT, false>), dim3((unsigned)blocks), dim3(256), 0,
-                       s, static_cast<const EO*>(eo), K, H, w, scale, static_cast<const SH*>(sh),
-                       gl, static_cast<OUT*>(out), n_vec);
+  const EO* eo_p = static_cast<const EO*>(eo);
+  const SH* sh_p = static_cast<const SH*>(sh);
+  OUT* out_p = static_cast<OUT*>(out);
+  void* args[] = {&eo_p, &K, &H, &w, &scale, &sh_p, &gl, &out_p, const_cast<long long*>(&n_vec)};
+  const void* kern = ((size_t)T * K * H * sizeof(EO) > ((size_t)256 << 20))
+                         ? reinterpret_cast<const void*>(combine_kernel<EO, SH, OUT, true>)
+                         : reinterpret_cast<const void*>(combine_kernel<EO, SH, OUT, false>);
+  (void)timed_launch(kern, dim3((unsigned)blocks), dim3(256), args, s);
 }
 
 template <typename EO, typename SH>

@@ -3,11 +3,15 @@
 * CPU: `--gpus N` with N > 1 exits with a message (one GPU only); the
   algorithmic byte and flop counts of the roofline follow their formulas for
   the bf16 and the keep-quant workloads.
+* CPU: the staged CPU baseline reports every stage, the host's CPU count and
+  one-thread times of the tiny and decode layers.
 * GPU: a short default run prints one JSON line carrying every field of the
   contract (metric, value, unit, steps, warmup, ms_per_step, dtype, config
   with the workload, roofline with bound / achieved / peak / frac / traffic,
-  cpu_baseline null when skipped), and the roofline fraction is achieved over
-  peak.
+  cpu_baseline null when skipped) for the skewed 8192-token layer, with the
+  MFMA roofline, the cold-cache combine, the routing check and the compact
+  runs of the decode, prefill and 256-expert layers; a decode run carries the
+  HBM roofline and the expert-parallel owner shares.
 """
 import json
 import os
@@ -52,12 +56,21 @@ def test_algorithmic_work_formulas():
         assert wbytes < gq["bytes"] < wbytes + 1_000_000
 
 
-@pytest.mark.gpu
-def test_default_run_prints_the_contract_line():
-    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3",
-                        "--warmup", "1", "--no-cpu-baseline", "--no-graph", "--no-fused",
-                        "--ep-share"],
-                       capture_output=True, text=True, cwd=ROOT, timeout=300)
+def test_cpu_baseline_reports_stages_and_cores():
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads as W
+    r = bench.cpu_baseline(W.make_inputs(1), 16, single_thread_workloads=(1,))
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
+    assert set(r["stages_s"]) == {"router_logits", "route", "gateup", "down", "shared", "combine"}
+    assert r["nproc"] == os.cpu_count() and 1 <= r["cores"] <= r["affinity_cpus"]
+    one = r["single_thread"]["tiny_T16_H64_E8_K2_I32_shared32"]
+    assert one["tokens_per_s"] > 0 and abs(sum(one["stages_s"].values()) - one["seconds"]) < 1e-9
+
+
+def _run(args):
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py")] + args,
+                       capture_output=True, text=True, cwd=ROOT, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
     assert len(lines) == 1
@@ -68,14 +81,66 @@ def test_default_run_prints_the_contract_line():
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
     assert d["unit"] == "tokens/s" and d["value"] > 0 and d["higher_is_better"] is True
+    assert d["cpu_baseline"] is None
+    return d
+
+
+def _check_combine(c, cfg):
+    T, K, H, I_s = cfg["T"], cfg["K"], cfg["H"], cfg["I_shared"]
+    assert c["bytes"] == T * K * H * 2 + T * H * 2 + (T * H * 2 + T * 4 if I_s else 0)
+    assert c["us"] > 0 and abs(c["gbs"] - c["bytes"] / (c["us"] * 1e-6) / 1e9) < 1e-6 * c["gbs"]
+    assert 0 < c["frac_of_hbm_peak"] < 1.2
+
+
+@pytest.mark.gpu
+def test_default_run_is_the_skewed_layer_with_compact_configs():
+    d = _run(["--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-graph", "--no-fused",
+              "--sub-steps", "2"])
+    assert d["config"]["workload"] == "skewed_T8192_H4096_E128_K8_I1536"
+    roof = d["roofline"]
+    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert k in roof, k
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == 2500.0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-9 and 0 < roof["frac"] < 1
+    gu_us = d["grouped_gemm"]["gateup_us"]
+    assert abs(roof["achieved"] - roof["algorithmic"]["flops_per_launch"] / gu_us / 1e6) < 1e-6 * roof["achieved"]
+    c = d["measured_ceilings"]
+    assert abs(roof["frac_of_measured"] - roof["achieved"] / c["mfma_bf16_tflops"]) < 1e-9
+    _check_combine(d["combine"], d["config"])
+    rc = d["routing_check"]
+    assert rc["tokens"] == 8192 and 0 <= rc["logit_max_abs_err"] < 1e-3
+    assert rc["tokens_whose_topk_set_differs_from_f64"] <= rc["tokens_with_gap_within_2x_err"]
+    subs = d["configs"]
+    assert set(subs) == {"decode_T32_H2048_E128_K8_I768", "prefill_T4096_H2048_E128_K8_I768",
+                         "shared_T512_H2048_E256_K8_I512_shared512"}
+    # the prefill gate-up's intensity (about 237 flop/B) sits below the ridge
+    # of 2.5 PFLOP/s over 8 TB/s (312.5 flop/B): HBM-bound by the roofline
+    bounds = {"decode_T32_H2048_E128_K8_I768": "hbm", "prefill_T4096_H2048_E128_K8_I768": "hbm",
+              "shared_T512_H2048_E256_K8_I512_shared512": "hbm"}
+    for name, r in subs.items():
+        assert r["tokens_per_s"] > 0 and r["gateup_us"] > 0 and r["down_us"] > 0
+        assert r["roofline"]["bound"] == bounds[name]
+        assert abs(r["roofline"]["frac"] - r["roofline"]["achieved"] / r["roofline"]["peak"]) < 1e-9
+        assert (r["roofline"]["flop_per_byte"] < 312.5) == (r["roofline"]["bound"] == "hbm")
+        assert abs(r["roofline"]["frac_of_mfma_peak"] * 2500.0 - r["roofline"]["tflops"]) < 1e-6
+        T = int(name.split("_T")[1].split("_")[0])
+        H = int(name.split("_H")[1].split("_")[0])
+        K = int(name.split("_K")[1].split("_")[0])
+        _check_combine(r["combine"], {"T": T, "K": K, "H": H, "I_shared": 512 if "shared512" in name else 0})
+
+
+@pytest.mark.gpu
+def test_decode_run_prints_the_contract_line():
+    d = _run(["--workload", "2", "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
+              "--no-graph", "--no-fused", "--ep-share"])
     assert d["config"]["workload"].startswith("decode_T32")
+    assert d["configs"] is None
     roof = d["roofline"]
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in roof, k
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-9
     assert 0 < roof["frac"] < 1
-    assert d["cpu_baseline"] is None
     # the chip's own ceilings from the library's micro-kernels, and the same
     # achieved figure against the measured read ceiling
     c = d["measured_ceilings"]
