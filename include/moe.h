@@ -144,11 +144,48 @@ typedef enum {
  * invalid arguments: E, R, K < 1, K not a multiple of 8, R odd for GATEUP).
  * moe_pack_weights converts w (bf16 [E, R, K], 16-byte aligned, device) into
  * packed (device, 16-byte aligned, moe_packed_weight_bytes bytes), stream-
- * ordered like every call. Limits: E <= 1024, R * K below 2^30 elements.
+ * ordered like every call, and fills the host descriptor *desc (not NULL)
+ * that the grouped GEMMs take in place of a bare weight pointer. Limits:
+ * E <= 1024, R * K below 2^30 elements. On any refusal *desc is left as it
+ * was.
  */
 size_t moe_packed_weight_bytes(int E, int R, int K, moe_pack_kind kind);
+
+/* The layout tag of a descriptor filled by moe_pack_weights. */
+#define MOE_WEIGHTS_PACKED_V1 0x4D4F4531u
+
+/*
+ * Host-side descriptor of a packed expert weight set: the weight argument of
+ * moe_grouped_gemm_gateup_silu, moe_grouped_gemm_down and
+ * moe_fused_expert_ffn. The row-major W_gu [E,2I,H] / W_d [E,H,I] of the
+ * pages cannot be read by these kernels, and a bare device pointer cannot
+ * say which layout it holds; so the calls take this descriptor, which only
+ * moe_pack_weights (and moe_weights_slice) fill, and refuse with
+ * MOE_E_INVALID and a message naming the argument any descriptor whose
+ * layout tag is not MOE_WEIGHTS_PACKED_V1, whose kind is not the call's
+ * (GATEUP for w_gu, PLAIN for w_d) or whose dimensions differ from the
+ * call's (E, 2I x H for w_gu, H x I for w_d). The caller owns the struct
+ * (plain host memory, read during the call only) and the device memory
+ * `data` points at.
+ */
+typedef struct {
+  uint32_t layout;       /* MOE_WEIGHTS_PACKED_V1 */
+  int32_t kind;          /* moe_pack_kind */
+  int32_t E, R, K;       /* experts, rows and reduced length of each expert's matrix */
+  int32_t reserved;
+  const void* data;      /* device: the packed blocks of expert 0 */
+  uint64_t expert_bytes; /* bytes of one expert's packed matrix */
+} moe_weights;
+
 moe_status moe_pack_weights(const uint16_t* w, int E, int R, int K, moe_pack_kind kind,
-                            uint16_t* packed, moe_stream_t stream);
+                            uint16_t* packed, moe_weights* desc, moe_stream_t stream);
+
+/* Experts [e0, e1) of a packed weight set as a descriptor of their own,
+ * viewing the same device memory (each expert's packed matrix is
+ * contiguous): the block of experts one rank owns when experts are split
+ * across GPUs. Host only, no launch. MOE_E_INVALID for a descriptor not
+ * filled by moe_pack_weights, MOE_E_SHAPE unless 0 <= e0 < e1 <= w->E. */
+moe_status moe_weights_slice(const moe_weights* w, int e0, int e1, moe_weights* out);
 
 /*
  * Router / gate logits helper (not a contract step; the router itself is the
@@ -238,17 +275,17 @@ moe_status moe_route_scored(const float* logits, int T, int E, int K, moe_score 
  *   gu[j]    = bf16( f32( x[t] . w_gu[e,j] ) )          j < 2I   (N1)
  *   act[q,i] = bf16( silu(gu[i]) * gu[I+i] ),  silu(g) = g / (1 + exp(-g))
  *   x      bf16 [T,H], 16-byte aligned
- *   w_gu   the gate-up weights W_gu [E,2I,H] (gate rows [0,I), up rows
- *          [I,2I)) packed by moe_pack_weights(..., E, 2I, H, MOE_PACK_GATEUP),
- *          16-byte aligned
+ *   w_gu   descriptor of the gate-up weights W_gu [E,2I,H] (gate rows
+ *          [0,I), up rows [I,2I)) packed by moe_pack_weights(..., E, 2I, H,
+ *          MOE_PACK_GATEUP, ...); anything else is refused (see moe_weights)
  *   sorted_pairs, expert_offsets  as produced by moe_route(T, E, K); both
  *          NULL means identity rows (E must be 1 and K 1: a dense expert,
  *          e.g. the shared expert)
  *   act    bf16 [T*K, I] in sorted order, 16-byte aligned
  * Experts with no rows cost nothing. f32 accumulation on MFMA.
  */
-moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w_gu,
-                                        int E, int I, const int32_t* sorted_pairs,
+moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H,
+                                        const moe_weights* w_gu, int E, int I, const int32_t* sorted_pairs,
                                         const int32_t* expert_offsets, int K, uint16_t* act,
                                         moe_stream_t stream);
 
@@ -258,14 +295,15 @@ moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const u
  *   y = f32( act[q] . w_d[e,h] );  expert_out[p,h] = bf16( y * pair_w[p] )
  *   stored at pair row p = sorted_pairs[q], so expert_out is [T,K,H].
  *   act    bf16 [P,I] in sorted order, 16-byte aligned
- *   w_d    the down weights W_d [E,H,I] packed by moe_pack_weights(..., E, H, I,
- *          MOE_PACK_PLAIN), 16-byte aligned
+ *   w_d    descriptor of the down weights W_d [E,H,I] packed by
+ *          moe_pack_weights(..., E, H, I, MOE_PACK_PLAIN, ...); anything
+ *          else is refused (see moe_weights)
  *   sorted_pairs, expert_offsets  from moe_route, or both NULL (identity, E=1)
  *   pair_w f32 [P] (= topk_w viewed flat) or NULL for no multiply
  *   expert_out bf16 [P,H], 16-byte aligned
  */
-moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const uint16_t* w_d, int E,
-                                 int H, const int32_t* sorted_pairs,
+moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const moe_weights* w_d,
+                                 int E, int H, const int32_t* sorted_pairs,
                                  const int32_t* expert_offsets, const float* pair_w,
                                  uint16_t* expert_out, moe_stream_t stream);
 
@@ -301,7 +339,8 @@ size_t moe_fused_expert_ffn_workspace_bytes(int T, int E, int K, int grouped);
  * agrees to the GEMM tolerance, not bit for bit), with no launch boundary
  * between the two: a row tile's down projection starts as soon as the act
  * rows of that tile are complete, while other tiles' gate-up work is still
- * running. Arguments as those two calls (packed w_gu and w_d, act [T*K, I]
+ * running. Arguments as those two calls (w_gu and w_d descriptors of packed
+ * weights, refused as there unless filled by moe_pack_weights, act [T*K, I]
  * and expert_out [T*K, H] bf16, pair_w may be NULL). Meant for decode (a few
  * rows per expert); it streams every tile, so with hundreds of rows per
  * expert the two calls are faster. On MI355X at 32 tokens x 128 experts
@@ -315,8 +354,8 @@ size_t moe_fused_expert_ffn_workspace_bytes(int T, int E, int K, int grouped);
  * bounded waits gave up (it cannot happen when the hardware dispatches
  * workgroups in order); expert_out is then invalid and ws must be zero-filled
  * again. MOE_E_WORKSPACE for a short, NULL or misaligned ws. */
-moe_status moe_fused_expert_ffn(const uint16_t* x, int T, int H, const uint16_t* w_gu,
-                                const uint16_t* w_d, int E, int I, const int32_t* sorted_pairs,
+moe_status moe_fused_expert_ffn(const uint16_t* x, int T, int H, const moe_weights* w_gu,
+                                const moe_weights* w_d, int E, int I, const int32_t* sorted_pairs,
                                 const int32_t* expert_offsets, int K, const float* pair_w,
                                 uint16_t* act, uint16_t* expert_out, void* ws, size_t ws_bytes,
                                 moe_stream_t stream);

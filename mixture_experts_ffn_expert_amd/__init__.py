@@ -46,6 +46,19 @@ STATUS = {0: "MOE_OK", 1: "MOE_E_INVALID", 2: "MOE_E_DTYPE", 3: "MOE_E_SHAPE",
 _p = ctypes.c_void_p
 _i = ctypes.c_int
 _st = ctypes.c_int
+
+MOE_WEIGHTS_PACKED_V1 = 0x4D4F4531
+
+
+class MoeWeights(ctypes.Structure):
+    """The C ABI's moe_weights: host descriptor of a packed expert weight set,
+    filled by moe_pack_weights / moe_weights_slice."""
+    _fields_ = [("layout", ctypes.c_uint32), ("kind", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("R", ctypes.c_int32), ("K", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("data", ctypes.c_void_p), ("expert_bytes", ctypes.c_uint64)]
+
+
+_wp = ctypes.POINTER(MoeWeights)
 SYMBOLS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_init": (_st, []),
@@ -54,20 +67,21 @@ SYMBOLS = {
     "moe_quantize_q8k": (_st, [_p, _i, _i, _p, _p]),
     "moe_q8_0_bytes": (ctypes.c_size_t, [_i, _i]),
     "moe_fused_expert_ffn_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
-    "moe_fused_expert_ffn": (_st, [_p, _i, _i, _p, _p, _i, _i, _p, _p, _i, _p, _p, _p, _p,
+    "moe_fused_expert_ffn": (_st, [_p, _i, _i, _wp, _wp, _i, _i, _p, _p, _i, _p, _p, _p, _p,
                                    ctypes.c_size_t, _p]),
     "moe_quantize_q8_0": (_st, [_p, _i, _i, _p, _p]),
     "moe_grouped_qgemm_gateup_silu": (_st, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _i, _p, _p]),
     "moe_grouped_qgemm_down": (_st, [_p, _i, _i, _p, _i, _i, _i, _p, _p, _p, _p, _p]),
-    "moe_pack_weights": (_st, [_p, _i, _i, _i, _i, _p, _p]),
+    "moe_pack_weights": (_st, [_p, _i, _i, _i, _i, _p, _wp, _p]),
+    "moe_weights_slice": (_st, [_wp, _i, _i, _wp]),
     "moe_time_next_gemm": (_st, [_p, _p]),
     "moe_router_logits": (_st, [_p, _i, _i, _p, _i, _p, _p, _p]),
     "moe_route_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
     "moe_route": (_st, [_p, _i, _i, _i, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
     "moe_route_scored": (_st, [_p, _i, _i, _i, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p,
                                ctypes.c_size_t, _p]),
-    "moe_grouped_gemm_gateup_silu": (_st, [_p, _i, _i, _p, _i, _i, _p, _p, _i, _p, _p]),
-    "moe_grouped_gemm_down": (_st, [_p, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p]),
+    "moe_grouped_gemm_gateup_silu": (_st, [_p, _i, _i, _wp, _i, _i, _p, _p, _i, _p, _p]),
+    "moe_grouped_gemm_down": (_st, [_p, _i, _i, _wp, _i, _i, _p, _p, _p, _p, _p]),
     "moe_combine_gate": (_st, [_p, _i, _i, _i, _i, _p, ctypes.c_float, _p, _i, _p, _p, _i, _p]),
     "moe_probe_out_values": (ctypes.c_size_t, []),
     "moe_probe_hbm_read": (_st, [_p, ctypes.c_size_t, _p, _p]),
@@ -304,10 +318,13 @@ MOE_PACK = {"plain": 0, "gateup": 1}
 class PackedWeights:
     """Expert weights in the library's packed layout (``moe_pack_weights``):
     ``data`` is the device buffer (uint8), ``E`` experts of a matrix [R, K]
-    packed as ``kind`` ("gateup": R = 2I gate and up rows; "plain")."""
+    packed as ``kind`` ("gateup": R = 2I gate and up rows; "plain");
+    ``desc`` is the library's descriptor of them, which the GEMM calls take."""
 
-    def __init__(self, data, E, R, K, kind):
-        self.data, self.E, self.R, self.K, self.kind = data, E, R, K, kind
+    def __init__(self, data, desc):
+        self.data, self.desc = data, desc
+        self.E, self.R, self.K = desc.E, desc.R, desc.K
+        self.kind = {v: k for k, v in MOE_PACK.items()}[desc.kind]
 
     def __repr__(self):
         return f"PackedWeights(E={self.E}, R={self.R}, K={self.K}, kind={self.kind!r})"
@@ -316,10 +333,10 @@ class PackedWeights:
         """Experts [e0, e1) as PackedWeights viewing the same memory (each
         expert's packed matrix is contiguous): the block of experts that one
         rank owns when experts are split across GPUs."""
-        if not (0 <= e0 < e1 <= self.E):
-            raise MoeError(3, f"expert range [{e0}, {e1}) outside [0, {self.E})")
-        per = self.data.numel() // self.E
-        return PackedWeights(self.data[e0 * per:e1 * per], e1 - e0, self.R, self.K, self.kind)
+        sub = MoeWeights()
+        _check(load().moe_weights_slice(ctypes.byref(self.desc), e0, e1, ctypes.byref(sub)))
+        per = int(self.desc.expert_bytes)
+        return PackedWeights(self.data[e0 * per:e1 * per], sub)
 
 
 def moe_packed_weight_bytes(E, R, K, kind):
@@ -343,8 +360,10 @@ def moe_pack_weights(w, kind, out=None, stream=None):
     if out is None:
         out = torch.empty((nbytes,), dtype=torch.uint8, device=w.device)
     _need(out, "packed", torch.uint8, shape=(nbytes,))
-    _check(load().moe_pack_weights(_ptr(w), E, R, K, MOE_PACK[kind], _ptr(out), _stream(stream)))
-    return PackedWeights(out, E, R, K, kind)
+    desc = MoeWeights()
+    _check(load().moe_pack_weights(_ptr(w), E, R, K, MOE_PACK[kind], _ptr(out), ctypes.byref(desc),
+                                   _stream(stream)))
+    return PackedWeights(out, desc)
 
 
 def _need_packed(pw, name, kind, R=None, K=None):
@@ -370,7 +389,7 @@ def moe_grouped_gemm_gateup_silu(x, w_gu, sorted_pairs, expert_offsets, K, act=N
     if act is None:
         act = torch.empty((T * K, I), dtype=torch.bfloat16, device=x.device)
     _need(act, "act", torch.bfloat16, shape=(T * K, I))
-    _check(load().moe_grouped_gemm_gateup_silu(_ptr(x), T, H, _ptr(w_gu.data), E, I,
+    _check(load().moe_grouped_gemm_gateup_silu(_ptr(x), T, H, ctypes.byref(w_gu.desc), E, I,
                                                _ptr(sorted_pairs), _ptr(expert_offsets), K,
                                                _ptr(act), _stream(stream)))
     return act
@@ -395,7 +414,8 @@ def moe_grouped_gemm_down(act, w_d, sorted_pairs, expert_offsets, pair_w, expert
     if expert_out is None:
         expert_out = torch.empty((P, H), dtype=torch.bfloat16, device=act.device)
     _need(expert_out, "expert_out", torch.bfloat16, shape=(P, H))
-    _check(load().moe_grouped_gemm_down(_ptr(act), P, I, _ptr(w_d.data), E, H, _ptr(sorted_pairs),
+    _check(load().moe_grouped_gemm_down(_ptr(act), P, I, ctypes.byref(w_d.desc), E, H,
+                                        _ptr(sorted_pairs),
                                         _ptr(expert_offsets), _ptr(pair_w), _ptr(expert_out),
                                         _stream(stream)))
     return expert_out
@@ -559,7 +579,8 @@ def moe_fused_expert_ffn(x, w_gu, w_d, sorted_pairs, expert_offsets, K, pair_w, 
     _need(act, "act", torch.bfloat16, shape=(P, I))
     _need(expert_out, "expert_out", torch.bfloat16, shape=(P, H))
     _check(load().moe_fused_expert_ffn(
-        _ptr(x), T, H, _ptr(w_gu.data), _ptr(w_d.data), E, I, _ptr(sorted_pairs), _ptr(expert_offsets), K,
+        _ptr(x), T, H, ctypes.byref(w_gu.desc), ctypes.byref(w_d.desc), E, I, _ptr(sorted_pairs),
+        _ptr(expert_offsets), K,
         _ptr(pair_w), _ptr(act), _ptr(expert_out), _ptr(workspace),
         workspace.numel() * 4, _stream(stream)))
     return act, expert_out

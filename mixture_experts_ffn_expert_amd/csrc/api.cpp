@@ -107,6 +107,32 @@ bool fits_packed(int R, int kdim, bool gateup) {
   return moe::packed_expert_bytes(R, kdim, gateup) < (size_t)(1u << 31);
 }
 
+// A packed weight descriptor as the grouped GEMMs need it: filled by
+// moe_pack_weights (layout tag), of the call's kind and dimensions, with an
+// aligned data pointer and the expert size the packed layout implies.
+moe_status check_weights(const char* fn, const char* arg, const moe_weights* w,
+                         moe_pack_kind kind, int E, int R, int K) {
+  if (w == nullptr) return fail(MOE_E_INVALID, "%s: %s is NULL", fn, arg);
+  if (w->layout != MOE_WEIGHTS_PACKED_V1)
+    return fail(MOE_E_INVALID,
+                "%s: %s is not a packed weight descriptor (layout tag 0x%08x); pack the row-major "
+                "weights with moe_pack_weights", fn, arg, w->layout);
+  const bool gu = kind == MOE_PACK_GATEUP;
+  if (w->kind != (int32_t)kind)
+    return fail(MOE_E_INVALID, "%s: %s was packed as %s, this call needs %s", fn, arg,
+                w->kind == MOE_PACK_GATEUP ? "MOE_PACK_GATEUP" : "MOE_PACK_PLAIN",
+                gu ? "MOE_PACK_GATEUP" : "MOE_PACK_PLAIN");
+  if (w->E != E || w->R != R || w->K != K)
+    return fail(MOE_E_INVALID, "%s: %s holds %d experts of [%d, %d], the call needs %d of [%d, %d]",
+                fn, arg, w->E, w->R, w->K, E, R, K);
+  if (w->expert_bytes != moe::packed_expert_bytes(R, K, gu))
+    return fail(MOE_E_INVALID, "%s: %s expert size %llu bytes does not match the packed layout",
+                fn, arg, (unsigned long long)w->expert_bytes);
+  if (w->data == nullptr || !aligned16(w->data))
+    return fail(MOE_E_INVALID, "%s: %s data is NULL or not 16-byte aligned", fn, arg);
+  return MOE_OK;
+}
+
 // Timing armed by moe_time_next_gemm applies to one GEMM call only: every
 // GEMM entry point disarms it on return, whether or not it launched.
 struct DisarmTiming {
@@ -178,9 +204,10 @@ size_t moe_packed_weight_bytes(int E, int R, int K, moe_pack_kind kind) {
 }
 
 moe_status moe_pack_weights(const uint16_t* w, int E, int R, int K, moe_pack_kind kind,
-                            uint16_t* packed, moe_stream_t stream) {
+                            uint16_t* packed, moe_weights* desc, moe_stream_t stream) {
   const char* fn = "moe_pack_weights";
   clear_err();
+  REQUIRE_NONNULL(fn, desc);
   if (kind != MOE_PACK_PLAIN && kind != MOE_PACK_GATEUP)
     return fail(MOE_E_INVALID, "%s: kind=%d is not MOE_PACK_PLAIN or MOE_PACK_GATEUP", fn,
                 (int)kind);
@@ -194,8 +221,36 @@ moe_status moe_pack_weights(const uint16_t* w, int E, int R, int K, moe_pack_kin
   REQUIRE_PTR(fn, packed);
   moe_status st = check_device(fn);
   if (st != MOE_OK) return st;
-  return hip_status(fn, moe::launch_pack(w, E, R, K, kind == MOE_PACK_GATEUP ? 1 : 0, packed,
-                                         static_cast<hipStream_t>(stream)));
+  st = hip_status(fn, moe::launch_pack(w, E, R, K, kind == MOE_PACK_GATEUP ? 1 : 0, packed,
+                                       static_cast<hipStream_t>(stream)));
+  if (st != MOE_OK) return st;
+  moe_weights d{};
+  d.layout = MOE_WEIGHTS_PACKED_V1;
+  d.kind = (int32_t)kind;
+  d.E = E;
+  d.R = R;
+  d.K = K;
+  d.data = packed;
+  d.expert_bytes = moe::packed_expert_bytes(R, K, kind == MOE_PACK_GATEUP);
+  *desc = d;
+  return MOE_OK;
+}
+
+moe_status moe_weights_slice(const moe_weights* w, int e0, int e1, moe_weights* out) {
+  const char* fn = "moe_weights_slice";
+  clear_err();
+  REQUIRE_NONNULL(fn, w);
+  REQUIRE_NONNULL(fn, out);
+  if (w->layout != MOE_WEIGHTS_PACKED_V1)
+    return fail(MOE_E_INVALID, "%s: w is not a packed weight descriptor (layout tag 0x%08x)", fn,
+                w->layout);
+  if (e0 < 0 || e1 <= e0 || e1 > w->E)
+    return fail(MOE_E_SHAPE, "%s: expert range [%d, %d) outside [0, %d)", fn, e0, e1, w->E);
+  moe_weights d = *w;
+  d.E = e1 - e0;
+  d.data = static_cast<const unsigned char*>(w->data) + (size_t)e0 * w->expert_bytes;
+  *out = d;
+  return MOE_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -501,7 +556,7 @@ moe_status moe_route_scored(const float* logits, int T, int E, int K, moe_score 
                                    static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const uint16_t* w_gu,
+moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const moe_weights* w_gu,
                                         int E, int I, const int32_t* sorted_pairs,
                                         const int32_t* expert_offsets, int K, uint16_t* act,
                                         moe_stream_t stream) {
@@ -525,17 +580,19 @@ moe_status moe_grouped_gemm_gateup_silu(const uint16_t* x, int T, int H, const u
     return fail(MOE_E_SHAPE, "%s: x exceeds 2^30 elements, one expert's packed w_gu 2^31 bytes, or T*K*I 2^31",
                 fn);
   if (T == 0) return MOE_OK;
-  REQUIRE_PTR(fn, x);
-  REQUIRE_PTR(fn, w_gu);
-  REQUIRE_PTR(fn, act);
-  moe_status st = check_device(fn);
+  moe_status st = check_weights(fn, "w_gu", w_gu, MOE_PACK_GATEUP, E, 2 * I, H);
   if (st != MOE_OK) return st;
-  return hip_status(fn, moe::launch_gateup_silu(x, T, H, w_gu, E, I, sorted_pairs, expert_offsets,
-                                                K, act, static_cast<hipStream_t>(stream)));
+  REQUIRE_PTR(fn, x);
+  REQUIRE_PTR(fn, act);
+  st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_gateup_silu(x, T, H, static_cast<const uint16_t*>(w_gu->data),
+                                                E, I, sorted_pairs, expert_offsets, K, act,
+                                                static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const uint16_t* w_d, int E,
-                                 int H, const int32_t* sorted_pairs,
+moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const moe_weights* w_d,
+                                 int E, int H, const int32_t* sorted_pairs,
                                  const int32_t* expert_offsets, const float* pair_w,
                                  uint16_t* expert_out, moe_stream_t stream) {
   const char* fn = "moe_grouped_gemm_down";
@@ -554,13 +611,15 @@ moe_status moe_grouped_gemm_down(const uint16_t* act, int P, int I, const uint16
     return fail(MOE_E_SHAPE,
                 "%s: act exceeds 2^30 elements, one expert's packed w_d 2^31 bytes, or P*H 2^31", fn);
   if (P == 0) return MOE_OK;
-  REQUIRE_PTR(fn, act);
-  REQUIRE_PTR(fn, w_d);
-  REQUIRE_PTR(fn, expert_out);
-  moe_status st = check_device(fn);
+  moe_status st = check_weights(fn, "w_d", w_d, MOE_PACK_PLAIN, E, H, I);
   if (st != MOE_OK) return st;
-  return hip_status(fn, moe::launch_down(act, P, I, w_d, E, H, sorted_pairs, expert_offsets,
-                                         pair_w, expert_out, static_cast<hipStream_t>(stream)));
+  REQUIRE_PTR(fn, act);
+  REQUIRE_PTR(fn, expert_out);
+  st = check_device(fn);
+  if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_down(act, P, I, static_cast<const uint16_t*>(w_d->data), E, H,
+                                         sorted_pairs, expert_offsets, pair_w, expert_out,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_fused_expert_ffn_workspace_bytes(int T, int E, int K, int grouped) {
@@ -568,8 +627,8 @@ size_t moe_fused_expert_ffn_workspace_bytes(int T, int E, int K, int grouped) {
   return (size_t)moe::fused_ffn_workspace_ints(T * K, E, grouped != 0) * 4;
 }
 
-moe_status moe_fused_expert_ffn(const uint16_t* x, int T, int H, const uint16_t* w_gu,
-                                const uint16_t* w_d, int E, int I, const int32_t* sorted_pairs,
+moe_status moe_fused_expert_ffn(const uint16_t* x, int T, int H, const moe_weights* w_gu,
+                                const moe_weights* w_d, int E, int I, const int32_t* sorted_pairs,
                                 const int32_t* expert_offsets, int K, const float* pair_w,
                                 uint16_t* act, uint16_t* expert_out, void* ws, size_t ws_bytes,
                                 moe_stream_t stream) {
@@ -598,16 +657,20 @@ moe_status moe_fused_expert_ffn(const uint16_t* x, int T, int H, const uint16_t*
   if (T > 0 && ws_bytes < need)
     return fail(MOE_E_WORKSPACE, "%s: workspace of %zu bytes < %zu required", fn, ws_bytes, need);
   if (T == 0) return MOE_OK;
+  moe_status st = check_weights(fn, "w_gu", w_gu, MOE_PACK_GATEUP, E, 2 * I, H);
+  if (st != MOE_OK) return st;
+  st = check_weights(fn, "w_d", w_d, MOE_PACK_PLAIN, E, H, I);
+  if (st != MOE_OK) return st;
   if (ws == nullptr || (uintptr_t)ws % 4 != 0)
     return fail(MOE_E_WORKSPACE, "%s: ws is NULL or not 4-byte aligned (%zu bytes needed)", fn, need);
   REQUIRE_PTR(fn, x);
-  REQUIRE_PTR(fn, w_gu);
-  REQUIRE_PTR(fn, w_d);
   REQUIRE_PTR(fn, act);
   REQUIRE_PTR(fn, expert_out);
-  moe_status st = check_device(fn);
+  st = check_device(fn);
   if (st != MOE_OK) return st;
-  return hip_status(fn, moe::launch_fused_ffn(x, T, H, w_gu, w_d, E, I, sorted_pairs,
+  return hip_status(fn, moe::launch_fused_ffn(x, T, H, static_cast<const uint16_t*>(w_gu->data),
+                                              static_cast<const uint16_t*>(w_d->data), E, I,
+                                              sorted_pairs,
                                               expert_offsets, K, pair_w, act, expert_out,
                                               static_cast<int*>(ws),
                                               static_cast<hipStream_t>(stream)));

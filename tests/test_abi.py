@@ -22,6 +22,22 @@ A2 = ctypes.c_void_p(0x20000)
 MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
 
 
+def _desc(kind, E, R, K, data=0x40000, layout=None, expert_bytes=None):
+    """A weight descriptor as moe_pack_weights fills it (host memory only)."""
+    d = moe.MoeWeights()
+    d.layout = moe.MOE_WEIGHTS_PACKED_V1 if layout is None else layout
+    d.kind, d.E, d.R, d.K = kind, E, R, K
+    d.data = data
+    nkb = (K + 31) // 32
+    per = ((R // 2 + 15) // 16) * nkb * 2 * 1024 if kind == 1 else ((R + 15) // 16) * nkb * 1024
+    d.expert_bytes = per if expert_bytes is None else expert_bytes
+    return ctypes.byref(d)
+
+
+GU = _desc(1, 8, 32, 16)          # W_gu [8, 2*16, 16] packed
+DN = _desc(0, 8, 16, 16)          # W_d [8, 16, 16] packed
+
+
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
@@ -87,16 +103,60 @@ def test_route_null_outputs_refused(lib):
 
 def test_gemm_refusals(lib):
     f = lib.moe_grouped_gemm_gateup_silu
-    assert f(A, 4, 12, A, 8, 16, A, A, 2, A, None) == 3 and "H=12" in _err(lib)
-    assert f(A, 4, 16, A, 8, 12, A, A, 2, A, None) == 3 and "I=12" in _err(lib)
-    assert f(A, 4, 16, A, 8, 16, A, None, 2, A, None) == 1 and "both" in _err(lib)
-    assert f(A, 4, 16, A, 8, 16, None, None, 2, A, None) == 1 and "identity" in _err(lib)
-    assert f(MIS, 4, 16, A, 8, 16, A, A, 2, A, None) == 1 and "aligned" in _err(lib)
+    assert f(A, 4, 12, GU, 8, 16, A, A, 2, A, None) == 3 and "H=12" in _err(lib)
+    assert f(A, 4, 16, GU, 8, 12, A, A, 2, A, None) == 3 and "I=12" in _err(lib)
+    assert f(A, 4, 16, GU, 8, 16, A, None, 2, A, None) == 1 and "both" in _err(lib)
+    assert f(A, 4, 16, GU, 8, 16, None, None, 2, A, None) == 1 and "identity" in _err(lib)
+    assert f(MIS, 4, 16, GU, 8, 16, A, A, 2, A, None) == 1 and "aligned" in _err(lib)
     assert f(A, 4, 16, None, 8, 16, A, A, 2, A, None) == 1 and "w_gu" in _err(lib)
     d = lib.moe_grouped_gemm_down
-    assert d(A, 8, 16, A, 8, 20, A, A, None, A, None) == 3 and "H=20" in _err(lib)
-    assert d(A, 8, 16, A, 8, 16, None, None, None, A, None) == 1 and "identity" in _err(lib)
-    assert d(A, 8, 16, A, 1, 16, None, None, None, MIS, None) == 1 and "expert_out" in _err(lib)
+    assert d(A, 8, 16, DN, 8, 20, A, A, None, A, None) == 3 and "H=20" in _err(lib)
+    assert d(A, 8, 16, DN, 8, 16, None, None, None, A, None) == 1 and "identity" in _err(lib)
+    dn1 = _desc(0, 1, 16, 16)
+    assert d(A, 8, 16, dn1, 1, 16, None, None, None, MIS, None) == 1 and "expert_out" in _err(lib)
+
+
+def test_unpacked_weights_refused_by_name(lib):
+    """The GEMM calls take a descriptor that moe_pack_weights fills; the
+    pages' row-major weights (a descriptor without the packed layout tag),
+    the other kind, other dimensions or a wrong expert size are refused
+    before any launch, naming the argument."""
+    f = lib.moe_grouped_gemm_gateup_silu
+    d = lib.moe_grouped_gemm_down
+    row_major = _desc(1, 8, 32, 16, layout=0)
+    assert f(A, 4, 16, row_major, 8, 16, A, A, 2, A, None) == 1
+    m = _err(lib)
+    assert "w_gu" in m and "not a packed weight descriptor" in m and "moe_pack_weights" in m
+    assert d(A, 8, 16, _desc(0, 8, 16, 16, layout=0x12345678), 8, 16, A, A, None, A, None) == 1
+    assert "w_d" in _err(lib) and "0x12345678" in _err(lib)
+    assert f(A, 4, 16, DN, 8, 16, A, A, 2, A, None) == 1 and "MOE_PACK_GATEUP" in _err(lib)
+    assert d(A, 8, 16, GU, 8, 16, A, A, None, A, None) == 1 and "MOE_PACK_PLAIN" in _err(lib)
+    assert f(A, 4, 16, GU, 4, 16, A, A, 2, A, None) == 1 and "8 experts" in _err(lib)
+    assert f(A, 4, 32, GU, 8, 16, A, A, 2, A, None) == 1 and "[32, 16]" in _err(lib)
+    assert d(A, 8, 16, DN, 8, 24, A, A, None, A, None) == 1 and "w_d" in _err(lib)
+    bad_size = _desc(1, 8, 32, 16, expert_bytes=1024)
+    assert f(A, 4, 16, bad_size, 8, 16, A, A, 2, A, None) == 1 and "expert size" in _err(lib)
+    assert f(A, 4, 16, _desc(1, 8, 32, 16, data=0x40008), 8, 16, A, A, 2, A, None) == 1
+    assert "data" in _err(lib)
+    assert f(A, 4, 16, _desc(1, 8, 32, 16, data=0), 8, 16, A, A, 2, A, None) == 1
+    # the fused FFN checks both
+    need = lib.moe_fused_expert_ffn_workspace_bytes(4, 8, 2, 1)
+    assert lib.moe_fused_expert_ffn(A, 4, 16, row_major, DN, 8, 16, A, A, 2, A, A, A, A, need,
+                                    None) == 1 and "w_gu" in _err(lib)
+    assert lib.moe_fused_expert_ffn(A, 4, 16, GU, GU, 8, 16, A, A, 2, A, A, A, A, need,
+                                    None) == 1 and "w_d" in _err(lib)
+
+
+def test_weights_slice(lib):
+    W = _desc(1, 8, 32, 16, data=0x100000)
+    per = W._obj.expert_bytes
+    out = moe.MoeWeights()
+    assert lib.moe_weights_slice(W, 2, 5, ctypes.byref(out)) == 0
+    assert (out.E, out.R, out.K, out.kind) == (3, 32, 16, 1)
+    assert out.data == 0x100000 + 2 * per and out.layout == moe.MOE_WEIGHTS_PACKED_V1
+    for e0, e1 in [(-1, 2), (3, 3), (5, 2), (0, 9)]:
+        assert lib.moe_weights_slice(W, e0, e1, ctypes.byref(out)) == 3 and "range" in _err(lib)
+    assert lib.moe_weights_slice(_desc(1, 8, 32, 16, layout=0), 0, 1, ctypes.byref(out)) == 1
     r = lib.moe_router_logits
     assert r(A, 4, 10, A, 8, None, A, None) == 3
     assert r(A, 4, 16, A, 0, None, A, None) == 3
@@ -117,8 +177,8 @@ def test_combine_scale_and_gate_refusals(lib):
 def test_zero_tokens_is_a_no_op(lib):
     assert lib.moe_combine_gate(None, 1, 0, 2, 8, None, 1.0, None, 1, None, None, 1, None) == 0
     assert lib.moe_route(None, 0, 8, 2, None, None, A, None, None, 0, None) == 0
-    assert lib.moe_grouped_gemm_gateup_silu(None, 0, 16, None, 8, 16, A, A, 2, None, None) == 0
-    assert lib.moe_grouped_gemm_down(None, 0, 16, None, 8, 16, A, A, None, None, None) == 0
+    assert lib.moe_grouped_gemm_gateup_silu(None, 0, 16, GU, 8, 16, A, A, 2, None, None) == 0
+    assert lib.moe_grouped_gemm_down(None, 0, 16, DN, 8, 16, A, A, None, None, None) == 0
     assert lib.moe_router_logits(None, 0, 16, None, 8, None, None, None) == 0
     assert _err(lib) == ""
 
@@ -173,7 +233,7 @@ def test_refused_gemm_call_disarms_timing(lib):
     # armed with dummy handles: a refused GEMM call must disarm, so the next
     # valid call never touches them (here the next call is refused too)
     assert lib.moe_time_next_gemm(A, A2) == 0
-    assert lib.moe_grouped_gemm_down(A, 8, 16, A, 8, 20, A, A, None, A, None) == 3
+    assert lib.moe_grouped_gemm_down(A, 8, 16, DN, 8, 20, A, A, None, A, None) == 3
     assert lib.moe_router_logits(None, 0, 16, None, 8, None, None, None) == 0
 
 
@@ -205,11 +265,15 @@ def test_packed_weight_bytes(lib):
 
 
 def test_pack_refusals(lib):
-    assert lib.moe_pack_weights(A, 2, 40, 12, 0, A2, None) == 3 and "K=12" in _err(lib)
-    assert lib.moe_pack_weights(A, 2, 41, 16, 1, A2, None) == 3 and "even" in _err(lib)
-    assert lib.moe_pack_weights(A, 2, 40, 16, 2, A2, None) == 1 and "kind" in _err(lib)
-    assert lib.moe_pack_weights(MIS, 2, 40, 16, 0, A2, None) == 1 and "aligned" in _err(lib)
-    assert lib.moe_pack_weights(A, 2, 40, 16, 0, None, None) == 1 and "packed" in _err(lib)
+    d = moe.MoeWeights()
+    D = ctypes.byref(d)
+    assert lib.moe_pack_weights(A, 2, 40, 12, 0, A2, D, None) == 3 and "K=12" in _err(lib)
+    assert lib.moe_pack_weights(A, 2, 41, 16, 1, A2, D, None) == 3 and "even" in _err(lib)
+    assert lib.moe_pack_weights(A, 2, 40, 16, 2, A2, D, None) == 1 and "kind" in _err(lib)
+    assert lib.moe_pack_weights(MIS, 2, 40, 16, 0, A2, D, None) == 1 and "aligned" in _err(lib)
+    assert lib.moe_pack_weights(A, 2, 40, 16, 0, None, D, None) == 1 and "packed" in _err(lib)
+    assert lib.moe_pack_weights(A, 2, 40, 16, 0, A2, None, None) == 1 and "desc" in _err(lib)
+    assert d.layout == 0                       # refusals leave the descriptor untouched
 
 
 def test_keepquant_refusals(lib):
@@ -246,15 +310,16 @@ def test_fused_ffn_workspace_and_refusals(lib):
     assert wb(0, 8, 2, 1) == 0 and wb(4, 0, 1, 1) == 0
     f = lib.moe_fused_expert_ffn
     need = wb(4, 8, 2, 1)
-    #     x  T  H    w_gu w_d E  I   sorted offs K  pair_w act eo  ws  ws_bytes
-    assert f(A, 4, 256, A2, A2, 8, 64, A, A, 2, A, A, A, A, need - 4, None) == 4
+    G, D = _desc(1, 8, 128, 256), _desc(0, 8, 256, 64)
+    #     x  T  H   w_gu w_d E  I   sorted offs K  pair_w act eo  ws  ws_bytes
+    assert f(A, 4, 256, G, D, 8, 64, A, A, 2, A, A, A, A, need - 4, None) == 4
     assert "workspace" in _err(lib)
-    assert f(A, 4, 256, A2, A2, 8, 64, A, A, 2, A, A, A, None, need, None) == 4
-    assert f(A, 4, 256, A2, A2, 8, 64, A, A, 9, A, A, A, A, need, None) == 3 and "K=9" in _err(lib)
-    assert f(A, 4, 256, A2, A2, 8, 64, None, A, 2, A, A, A, A, need, None) == 1
-    assert f(A, 4, 250, A2, A2, 8, 64, A, A, 2, A, A, A, A, need, None) == 3
-    assert f(A, 4, 256, A2, A2, 2, 64, None, None, 2, A, A, A, A, need, None) == 1
-    assert f(A, 4, 256, MIS, A2, 8, 64, A, A, 2, A, A, A, A, need, None) == 1
+    assert f(A, 4, 256, G, D, 8, 64, A, A, 2, A, A, A, None, need, None) == 4
+    assert f(A, 4, 256, G, D, 8, 64, A, A, 9, A, A, A, A, need, None) == 3 and "K=9" in _err(lib)
+    assert f(A, 4, 256, G, D, 8, 64, None, A, 2, A, A, A, A, need, None) == 1
+    assert f(A, 4, 250, G, D, 8, 64, A, A, 2, A, A, A, A, need, None) == 3
+    assert f(A, 4, 256, G, D, 2, 64, None, None, 2, A, A, A, A, need, None) == 1
+    assert f(MIS, 4, 256, G, D, 8, 64, A, A, 2, A, A, A, A, need, None) == 1
     assert "aligned" in _err(lib)
     assert f(None, 0, 256, None, None, 8, 64, A, A, 2, None, None, None, None, 0, None) == 0
 
@@ -289,11 +354,12 @@ def test_packed_weights_expert_block_views(lib):
     per = n // E
     assert per * E == n and per % 1024 == 0
     data = torch.arange(n, dtype=torch.int64).remainder(251).to(torch.uint8)
-    pw = moe.PackedWeights(data, E, R, K, "gateup")
+    desc = _desc(1, E, R, K, data=data.data_ptr())._obj
+    pw = moe.PackedWeights(data, desc)
     blk = pw.experts(2, 5)
     assert (blk.E, blk.R, blk.K, blk.kind) == (3, R, K, "gateup")
     assert blk.data.numel() == moe.moe_packed_weight_bytes(3, R, K, "gateup")
-    assert blk.data.data_ptr() == data.data_ptr() + 2 * per
+    assert blk.data.data_ptr() == data.data_ptr() + 2 * per == blk.desc.data
     assert torch.equal(blk.data, data[2 * per:5 * per])
     assert pw.experts(0, E).data.numel() == n
     for e0, e1 in [(-1, 2), (3, 3), (5, 2), (0, E + 1)]:
