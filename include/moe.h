@@ -226,6 +226,26 @@ moe_status moe_route(const float* logits, int T, int E, int K, int32_t* topk_ids
                      float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
                      void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/*
+ * For callers that cannot allocate (code under hipGraph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_route with the
+ * grouping scratch held by the library instead of a caller workspace. Same
+ * arguments (without ws, ws_bytes), results and errors as moe_route. The
+ * library holds 1 MiB of scratch per GPU in a static device array (kept
+ * until the process ends); T*K pairs over E experts need
+ * moe_route_workspace_bytes(T, E, K) bytes of it (4 per (1024-pair segment,
+ * expert)), so with E = 128 up to 2,097,152 pairs fit; larger sizes are
+ * refused with MOE_E_WORKSPACE. Nothing in the scratch needs to start at
+ * zero. It calls no allocator. Every call on one GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (on different streams, or from
+ * different host threads) race and must be ordered by the caller. The
+ * scratch's device address is looked up by moe_init (or by the first call on
+ * a device): call moe_init on each device before capturing this call.
+ */
+moe_status moe_route_noalloc(const float* logits, int T, int E, int K, int32_t* topk_ids,
+                             float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                             moe_stream_t stream);
+
 typedef enum {
   MOE_SCORE_SOFTMAX = 0, /* softmax over all E experts */
   MOE_SCORE_SIGMOID = 1  /* sigmoid of each logit */

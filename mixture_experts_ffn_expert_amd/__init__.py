@@ -30,7 +30,7 @@ __all__ = [
     "moe_fused_expert_ffn_workspace_bytes", "moe_fused_expert_ffn", "fused_ffn_status",
     "moe_grouped_qgemm_gateup_silu", "moe_grouped_qgemm_down", "MOE_Q4_K", "MOE_Q5_K",
     "MOE_Q6_K", "MOE_Q8_0", "MOE_QTYPE", "KQ_BLOCK", "moe_router_logits", "moe_route",
-    "moe_route_workspace_bytes", "moe_route_scored", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
+    "moe_route_workspace_bytes", "moe_route_noalloc", "moe_route_scored", "moe_grouped_gemm_gateup_silu", "moe_grouped_gemm_down",
     "moe_combine_gate", "moe_layer", "moe_time_next_gemm", "moe_probe_out_values",
     "moe_probe_hbm_read", "moe_probe_mfma_bf16", "moe_probe_mfma_flops", "MOE_F32", "MOE_BF16", "MOE_F16", "SYMBOLS",
 ]
@@ -78,6 +78,7 @@ SYMBOLS = {
     "moe_router_logits": (_st, [_p, _i, _i, _p, _i, _p, _p, _p]),
     "moe_route_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
     "moe_route": (_st, [_p, _i, _i, _i, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]),
+    "moe_route_noalloc": (_st, [_p, _i, _i, _i, _p, _p, _p, _p, _p]),
     "moe_route_scored": (_st, [_p, _i, _i, _i, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p,
                                ctypes.c_size_t, _p]),
     "moe_grouped_gemm_gateup_silu": (_st, [_p, _i, _i, _wp, _i, _i, _p, _p, _i, _p, _p]),
@@ -265,6 +266,22 @@ def moe_route(logits, K, topk_ids=None, topk_w=None, expert_offsets=None, sorted
     _check(load().moe_route(_ptr(logits), T, E, K, _ptr(topk_ids), _ptr(topk_w),
                             _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(workspace), ws_bytes,
                             _stream(stream)))
+    return topk_ids, topk_w, expert_offsets, sorted_pairs
+
+
+def moe_route_noalloc(logits, K, topk_ids, topk_w, expert_offsets, sorted_pairs, stream=None):
+    """moe_route with the library's own grouping scratch: the caller passes
+    every output and nothing is allocated (for code under graph capture or
+    loops that must not allocate). Calls that overlap on one GPU race."""
+    import torch
+    _need(logits, "logits", torch.float32, 2)
+    T, E = logits.shape
+    _need(topk_ids, "topk_ids", torch.int32, shape=(T, K))
+    _need(topk_w, "topk_w", torch.float32, shape=(T, K))
+    _need(expert_offsets, "expert_offsets", torch.int32, shape=(E + 1,))
+    _need(sorted_pairs, "sorted_pairs", torch.int32, shape=(T * K,))
+    _check(load().moe_route_noalloc(_ptr(logits), T, E, K, _ptr(topk_ids), _ptr(topk_w),
+                                    _ptr(expert_offsets), _ptr(sorted_pairs), _stream(stream)))
     return topk_ids, topk_w, expert_offsets, sorted_pairs
 
 

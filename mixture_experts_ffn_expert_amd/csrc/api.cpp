@@ -147,7 +147,14 @@ const char* moe_last_error(void) { return g_err; }
 
 moe_status moe_init(void) {
   clear_err();
-  return check_device("moe_init");
+  moe_status st = check_device("moe_init");
+  if (st != MOE_OK) return st;
+  // the device address of moe_route_noalloc's scratch, once per device
+  void* p = nullptr;
+  const hipError_t e = moe::route_scratch(&p);
+  if (e != hipSuccess)
+    return fail(MOE_E_HIP, "moe_init: grouping scratch lookup failed: %s", hipGetErrorString(e));
+  return MOE_OK;
 }
 
 moe_status moe_time_next_gemm(void* start, void* stop) {
@@ -500,6 +507,39 @@ moe_status moe_route(const float* logits, int T, int E, int K, int32_t* topk_ids
   REQUIRE_NONNULL(fn, sorted_pairs);
   moe_status st = check_device(fn);
   if (st != MOE_OK) return st;
+  return hip_status(fn, moe::launch_route(logits, T, E, K, topk_ids, topk_w, expert_offsets,
+                                          sorted_pairs, ws, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_route_noalloc(const float* logits, int T, int E, int K, int32_t* topk_ids,
+                             float* topk_w, int32_t* expert_offsets, int32_t* sorted_pairs,
+                             moe_stream_t stream) {
+  const char* fn = "moe_route_noalloc";
+  clear_err();
+  if (T < 0) return fail(MOE_E_SHAPE, "%s: T=%d is negative", fn, T);
+  if (E < 1 || E > kMaxE) return fail(MOE_E_SHAPE, "%s: E=%d outside [1, %d]", fn, E, kMaxE);
+  if (K < 1 || K > E || K > kMaxK)
+    return fail(MOE_E_SHAPE, "%s: K=%d outside [1, min(E=%d, %d)]", fn, K, E, kMaxK);
+  if (!fits_i32((long long)T * E) || !fits_i32((long long)T * K))
+    return fail(MOE_E_SHAPE, "%s: T*E or T*K exceeds 2^31", fn);
+  const size_t need = moe_route_workspace_bytes(T, E, K);
+  if (need > moe::kRouteScratchBytes)
+    return fail(MOE_E_WORKSPACE,
+                "%s: T*K=%lld pairs over E=%d experts need %zu bytes of grouping scratch; the "
+                "library holds %zu (use moe_route with a caller workspace)",
+                fn, (long long)T * K, E, need, moe::kRouteScratchBytes);
+  REQUIRE_NONNULL(fn, expert_offsets);
+  if (T == 0) return MOE_OK;  // nothing routed; no output is written
+  REQUIRE_NONNULL(fn, logits);
+  REQUIRE_NONNULL(fn, topk_ids);
+  REQUIRE_NONNULL(fn, topk_w);
+  REQUIRE_NONNULL(fn, sorted_pairs);
+  moe_status st = check_device(fn);
+  if (st != MOE_OK) return st;
+  void* ws = nullptr;
+  const hipError_t e = moe::route_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(MOE_E_HIP, "%s: grouping scratch lookup failed: %s", fn, hipGetErrorString(e));
   return hip_status(fn, moe::launch_route(logits, T, E, K, topk_ids, topk_w, expert_offsets,
                                           sorted_pairs, ws, static_cast<hipStream_t>(stream)));
 }

@@ -24,6 +24,12 @@ hipError_t launch_pack(const uint16_t* w, int E, int R, int kdim, int gateup, ui
 
 // route.hip
 size_t route_workspace_bytes(int T, int E, int K);
+// The library-held grouping scratch of moe_route_noalloc: its size, and its
+// device address on the current device (looked up on the first call per
+// device and kept; devices 0 .. kRouteScratchDevices - 1).
+constexpr size_t kRouteScratchBytes = (size_t)1 << 20;
+constexpr int kRouteScratchDevices = 64;
+hipError_t route_scratch(void** out);
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                         int32_t* offsets, int32_t* sorted, void* ws, hipStream_t s);
 hipError_t launch_route_scored(const float* logits, int T, int E, int K, int sigmoid,

@@ -19,8 +19,17 @@
 //   in order, 64 pairs at a time, ranks equal experts inside the 64 by
 //   ballots, and scatters. No atomic decides an order, so the permutation is
 //   the stable one and is reproducible.
+#include <mutex>
+
 #include "device_math.h"
 #include "launch.h"
+
+// Grouping scratch held by the library for moe_route_noalloc: the
+// per-(segment, expert) counts of the segmented grouping, 4 bytes each, at
+// most kRouteScratchBytes. Each GPU the library runs on holds its own copy
+// until the process ends. Host code never uses this name as an address: it
+// takes the device address from hipGetSymbolAddress (route_scratch below).
+static __device__ __align__(256) int32_t scratch[moe::kRouteScratchBytes / 4];
 
 namespace moe {
 
@@ -553,6 +562,30 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, 
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_grouping(ids, T * K, E, offsets, sorted, ws, s);
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current and kept.
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kRouteScratchDevices] = {};
+}  // namespace
+
+hipError_t route_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kRouteScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_route_scored(const float* logits, int T, int E, int K, int sigmoid,

@@ -183,6 +183,21 @@ def test_zero_tokens_is_a_no_op(lib):
     assert _err(lib) == ""
 
 
+def test_route_noalloc_limits(lib):
+    """The library-held grouping scratch is 1 MiB: 4 bytes per (1024-pair
+    segment, expert). Sizes past it are refused before any launch, naming the
+    sizes; the other checks are moe_route's."""
+    f = lib.moe_route_noalloc
+    # E = 128: 2048 segments fit (2,097,152 pairs); one more pair does not
+    assert lib.moe_route_workspace_bytes(262144, 128, 8) == 1 << 20
+    assert f(A, 262145, 128, 8, A, A, A, A, None) == 4
+    m = _err(lib)
+    assert "moe_route_noalloc" in m and "2097160 pairs" in m and "1048576" in m
+    assert f(A, 4, 8, 9, A, A, A, A, None) == 3 and "K=9" in _err(lib)
+    assert f(A, 4, 8, 2, A, A, None, A, None) == 1 and "expert_offsets" in _err(lib)
+    assert f(None, 0, 8, 2, None, None, A, None, None) == 0 and _err(lib) == ""
+
+
 def test_route_workspace_query(lib):
     assert lib.moe_route_workspace_bytes(8192, 128, 8) == 64 * 128 * 4  # 1024-pair segments
     assert lib.moe_route_workspace_bytes(512, 128, 8) == 0
