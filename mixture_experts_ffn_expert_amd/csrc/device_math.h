@@ -21,18 +21,34 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// f32 -> bf16 bits, round to nearest even. NaN keeps sign and top payload and
-// gets the quiet bit; the carry of the rounding increment moves into the
-// exponent, so values past the largest bf16 become infinity.
+// f32 -> bf16 bits, round to nearest even: the conversion the compiler emits
+// for a float -> __bf16 cast on gfx950 (v_cvt_pk_bf16_f32, IEEE round to
+// nearest even, subnormals kept, values past the largest bf16 to infinity).
+// A NaN keeps its sign and top payload bits and gets the quiet bit, selected
+// without a branch.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rn = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+  const uint32_t qn = (u >> 16) | 0x0040u;
+  return (f != f) ? qn : rn;
 }
 
 // f32 rounded to bf16 and read back as f32 (one narrowing).
 __device__ __forceinline__ float round_bf16(float f) {
   return bf16_to_f32(f32_to_bf16(f));
+}
+
+// Two f32 values rounded to bf16 (nearest even) by one v_cvt_pk_bf16_f32 and
+// read back as f32: lo and hi. For a NaN input the result is a NaN whose
+// payload is the hardware's (the narrowing of the gate-up pair, N1, where
+// only the NaN-ness of a NaN can matter).
+__device__ __forceinline__ void round_bf16_pair(float& lo, float& hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  const uint32_t p = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b16x2_t));
+  lo = __uint_as_float(p << 16);
+  hi = __uint_as_float(p & 0xFFFF0000u);
 }
 
 // e^x in f32: Cody & Waite argument reduction (n = rint(x / ln2),

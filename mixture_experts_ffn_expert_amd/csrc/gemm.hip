@@ -804,7 +804,9 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   static_assert(BM % 16 == 0 && BN % 16 == 0, "swizzle period");
   static_assert(EPI != EPI_GATEUP || FN % 2 == 0, "gate-up pairs fragments");
   static_assert(EPI != EPI_F32, "logits use the streaming kernel");
-  static_assert(BM * CLD * 2 <= NS * STAGE, "output staging fits the ring");
+  // the bf16 output tile goes through the ring in NP passes of BM / NP rows
+  constexpr int NP = (BM * CLD * 2 <= NS * STAGE) ? 1 : 2;
+  static_assert((BM / NP) * CLD * 2 <= NS * STAGE && BM % (32 * NP) == 0, "output staging");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE];
   __shared__ int row_dest[BM];
   __shared__ float row_w[BM];
@@ -861,10 +863,11 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   constexpr int KBS = BK / 32;  // packed k blocks per stage
   uint32_t voff[IPW];
   int chunk[IPW];
+  static_assert((BM / RPL) % NW == 0, "A loads split evenly over the waves");
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
-    const int blk = wave * IPW + j;
-    if (blk * RPL < BM) {
+    const int blk = j * NW + wave;
+    if (j * NW * RPL < BM) {
       const int r = blk * RPL + lane / CPR;
       const int c = (lane % CPR) ^ ((r >> 1) & (CPR - 1));
       voff[j] = ((r < rows) ? a_row_off(g, row0 + r) : kOob) + c * 16;
@@ -887,19 +890,28 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
     }
   }
   const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  const uint32_t wave_lds = ring_base + (uint32_t)wave * 1024u;
   auto issue = [&](int slot, int k0) {
     const uint32_t soff_a = (uint32_t)k0 * 2u;
     const uint32_t soff_b = (uint32_t)(k0 / 32) * kb_stride<EPI>();
-    const bool full = k0 + BK <= g.kdim;
+    const uint32_t base = wave_lds + (uint32_t)slot * STAGE;
+    if (k0 + BK <= g.kdim) {
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int blk = wave * IPW + j;  // uniform
-      const uint32_t m0 = ring_base + slot * STAGE + blk * 1024;
-      const uint32_t vo = (full || k0 + chunk[j] < g.kdim) ? voff[j] : kOob;
-      if (blk * RPL < BM)
-        dma16(rsrc_a, m0, vo, soff_a);
-      else
-        dma16(rsrc_b, m0, vo, soff_b);
+      for (int j = 0; j < IPW; ++j) {
+        if (j * NW * RPL < BM)
+          dma16(rsrc_a, base + j * NW * 1024, voff[j], soff_a);
+        else
+          dma16(rsrc_b, base + j * NW * 1024, voff[j], soff_b);
+      }
+    } else {  // the k tail: chunks at or past kdim read as zero
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const uint32_t vo = (k0 + chunk[j] < g.kdim) ? voff[j] : kOob;
+        if (j * NW * RPL < BM)
+          dma16(rsrc_a, base + j * NW * 1024, vo, soff_a);
+        else
+          dma16(rsrc_b, base + j * NW * 1024, vo, soff_b);
+      }
     }
   };
 
@@ -1014,20 +1026,26 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   wait_barrier<0>();  // ring free for the output staging
 
   // Epilogue (as in tiled_kernel): bf16 results into LDS, then 16-byte row
-  // segments to the output rows.
+  // segments to the output rows, in NP passes of PR rows.
   uint16_t* smem = reinterpret_cast<uint16_t*>(ring);
+  constexpr int PR = BM / NP;
+#pragma unroll
+  for (int pass = 0; pass < NP; ++pass) {
+  if (pass > 0) __syncthreads();  // the previous pass's rows are out
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    if (((i * WM + wm) * 32) / PR != pass) continue;  // fragment rows lie in one pass
+    if (i >= nva) continue;  // wholly past the tile's last row: nothing to store
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int rr = (i * WM + wm) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      uint16_t* crow = smem + rr * CLD;
+      uint16_t* crow = smem + (rr - pass * PR) * CLD;
       if (EPI == EPI_GATEUP) {
 #pragma unroll
         for (int pp = 0; pp < FN / 2; ++pp) {
 #pragma clang fp contract(off)
-          const float gb = round_bf16(acc[i][2 * pp][r]);  // N1
-          const float ub = round_bf16(acc[i][2 * pp + 1][r]);
+          float gb = acc[i][2 * pp][r], ub = acc[i][2 * pp + 1][r];
+          round_bf16_pair(gb, ub);  // N1: narrow before the activation
           crow[wn * (TN / 2) + pp * 32 + r32] = (uint16_t)f32_to_bf16(silu_cw(gb) * ub);
         }
       } else {
@@ -1044,14 +1062,15 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   }
   __syncthreads();
   constexpr int CH = OUT_COLS / 8;
-  for (int idx = tid; idx < BM * CH; idx += NT) {
-    const int rr = idx / CH, c8 = (idx - rr * CH) * 8;
-    const int dest = row_dest[rr];
+  for (int idx = tid; idx < PR * CH; idx += NT) {
+    const int lr = idx / CH, c8 = (idx - lr * CH) * 8;
+    const int dest = row_dest[pass * PR + lr];
     const int col = n0 + c8;
     if (dest < 0 || col >= g.n_out) continue;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + rr * CLD + c8);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + lr * CLD + c8);
     *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(g.out) + (size_t)dest * g.n_out + col) =
         v;
+  }
   }
 }
 
@@ -1196,7 +1215,17 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
       g.slots = slots_for(g.P, g.E, BM, grouped);
       return run(tiled_dma_kernel<EPI, BM, BN, 2, 4, 4>, grid_for(g), 512, s, g);
     } else {
-      // down: 128 x 128 register-staged tiles, 4 workgroups per CU
+      if ((long long)(g.P / 320) * ((g.n_out + 255) / 256) >= 512) {
+        // down with enough 320 x 256 tiles to fill the chip: the gate-up's
+        // direct-to-LDS ring kernel, the output tile staged in two passes
+        // (skewed 8192-token layer 960 -> 930 us)
+        constexpr int BM = 320, BN = 256;
+        g.nblk = (g.n_out + BN - 1) / BN;
+        g.slots = slots_for(g.P, g.E, BM, grouped);
+        return run(tiled_dma_kernel<EPI, BM, BN, 2, 4, 4>, grid_for(g), 512, s, g);
+      }
+      // fewer (one expert-parallel owner's share): 128 x 128 register-staged
+      // tiles, 4 workgroups per CU
       constexpr int BM = 128, BN = 128;
       g.nblk = (g.n_out + BN - 1) / BN;
       g.slots = slots_for(g.P, g.E, BM, grouped);

@@ -108,3 +108,36 @@ def test_combine_gate_zero_gives_half_and_canary(gpu_lib):
     exp = (acc + O.f32_from_bf16(sd) * F32(0.5)).astype(F32)
     assert np.array_equal(bits(out), exp)
     assert torch.all(out_full[T * H:] == 12345.0).item(), "write past the output"
+
+
+def test_bf16_store_rounding_sweep(gpu_lib):
+    """The combine's f32 -> bf16 store against the oracle's round-to-nearest-
+    even on every bf16 high half with eight low-half classes (exact, smallest
+    step up, just below / at / just above the tie, the largest, and two
+    random), which covers ties to even, subnormals, the carry into the
+    exponent, overflow to infinity and NaN. K = 1, unweighted, scale 1, no
+    shared term: out = bf16(+0 + v). NaN outputs compare by position and
+    sign (the payload of an add's NaN result is the hardware's choice)."""
+    g = np.random.Generator(np.random.PCG64(77))
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = [0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF]
+    cols = [hi | lo for lo in lows] + [hi | g.integers(0, 1 << 16, hi.size, dtype=np.uint32)
+                                       for _ in range(2)]
+    u = np.stack(cols, axis=1).reshape(-1)                 # 524,288 patterns
+    T, H = 512, 1024
+    v = u.view(np.float32).reshape(T, H)
+    out = gpu_lib.moe_combine_gate(to_dev(v), T, 1, None, 1.0, None, None,
+                                   out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    got = bits(out).astype(np.uint32)
+    ref = O.combine_gate(v, T, 1, H, None, 1.0, None, None, eo_bf16=False, out_bf16=True)
+    ref = ref.astype(np.uint32)
+    nan_g = (got & 0x7F80) == 0x7F80
+    nan_g &= (got & 0x7F) != 0
+    nan_r = ((ref & 0x7F80) == 0x7F80) & ((ref & 0x7F) != 0)
+    assert np.array_equal(nan_g, nan_r), "NaN positions differ"
+    assert np.array_equal(got[nan_g] & 0x8000, ref[nan_r] & 0x8000), "NaN signs differ"
+    ok = ~nan_r
+    diff = int(np.count_nonzero(got[ok] != ref[ok]))
+    assert diff == 0, f"{diff} of {int(ok.sum())} non-NaN stores differ"
+    assert int(ok.sum()) > 500000
