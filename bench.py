@@ -839,6 +839,10 @@ def main():
             roof["frac_of_measured"] = roof["achieved"] / ceilings["hbm_read_gbs"]
         elif not keepquant:
             roof["frac_of_measured"] = roof["achieved"] / ceilings["mfma_bf16_tflops"]
+    # the shader clock the chip ran the timed steps at (its power management
+    # lowers it under sustained MFMA load; the datasheet peak assumes 2.4 GHz)
+    sclk = (gpu_state or {}).get("sclk_mhz") or {}
+    roof["sclk_mhz_median"] = sclk.get("median")
     roof["kernel"] = (f"grouped keep-quant gate-up GEMM + SiLU-mul ({lay.wtype.upper()})"
                       if keepquant else "grouped gate-up GEMM + SiLU-mul")
     roof["algorithmic"] = {"bytes_per_launch": gu["bytes"], "flops_per_launch": gu["flops"],

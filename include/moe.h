@@ -364,16 +364,19 @@ size_t moe_fused_expert_ffn_workspace_bytes(int T, int E, int K, int grouped);
  * and expert_out [T*K, H] bf16, pair_w may be NULL). Meant for decode (a few
  * rows per expert); it streams every tile, so with hundreds of rows per
  * expert the two calls are faster. On MI355X at 32 tokens x 128 experts
- * (H 2048, I 768) it takes about 198 us against 115 + 59 us for the two
- * calls: its down phase has to take the gate-up's workgroup shape.
+ * (H 2048, I 768) it takes about 185 us against 104 + 53 us for the two
+ * calls (its down phase has to take the gate-up's 512-thread workgroup
+ * shape, where alone it runs best at 192 threads): it is kept for callers
+ * that want one launch, not for speed.
  * ws: moe_fused_expert_ffn_workspace_bytes(T, E, K, sorted_pairs != NULL)
  * bytes, 4-byte aligned, owned by the caller, zero-filled before its first
  * use. Every launch leaves the counters zero again, so the same ws serves the
  * next call on the same stream (calls that overlap on one ws race). Its last
  * int32 is a status word: nonzero after a launch means one of the kernel's
  * bounded waits gave up (it cannot happen when the hardware dispatches
- * workgroups in order); expert_out is then invalid and ws must be zero-filled
- * again. MOE_E_WORKSPACE for a short, NULL or misaligned ws. */
+ * workgroups in order); expert_out is then invalid, the counters are in
+ * doubt, and the whole ws must be zero-filled again before the next call.
+ * MOE_E_WORKSPACE for a short, NULL or misaligned ws. */
 moe_status moe_fused_expert_ffn(const uint16_t* x, int T, int H, const moe_weights* w_gu,
                                 const moe_weights* w_d, int E, int I, const int32_t* sorted_pairs,
                                 const int32_t* expert_offsets, int K, const float* pair_w,

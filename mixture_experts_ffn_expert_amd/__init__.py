@@ -569,7 +569,11 @@ def moe_fused_expert_ffn(x, w_gu, w_d, sorted_pairs, expert_offsets, K, pair_w, 
                          act=None, expert_out=None, stream=None):
     """Gate-up, SiLU-mul and down in one launch (packed w_gu, w_d).
     workspace: int32 tensor of moe_fused_expert_ffn_workspace_bytes bytes,
-    zero-filled before its first use (each launch leaves it zero)."""
+    zero-filled before its first use. A launch whose status word ends 0
+    (fused_ffn_status) leaves the counters zero for the next one; after a
+    nonzero status the results are invalid and the whole workspace must be
+    zero-filled again before it is reused. Slower than the two GEMM calls at
+    the decode shape (see moe.h); kept for callers that want one launch."""
     import torch
     _need(x, "x", torch.bfloat16, 2)
     _need_packed(w_gu, "w_gu", "gateup")

@@ -1349,6 +1349,12 @@ __global__ __launch_bounds__(64 * kFusedKS) void fused_ffn_kernel(FusedArgs fa) 
           }
           __builtin_amdgcn_s_sleep(8);
         }
+        // a wait that gave up elsewhere leaves every count of this launch in
+        // doubt (a late gate-up workgroup may add to a count already reset):
+        // give up too
+        if (st == 1 &&
+            __hip_atomic_load(fa.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+          st = 2;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
       go = st;
