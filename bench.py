@@ -124,7 +124,7 @@ def kernel_code_fingerprint():
 
 # committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries of the gate-up GEMM
 TRAFFIC_SUMMARIES = {2: "decode_gateup_hbm_traffic.md", 3: "prefill_gateup_hbm_traffic.md",
-                     5: "skewed_gateup_hbm_traffic.md"}
+                     4: "e256_gateup_hbm_traffic.md", 5: "skewed_gateup_hbm_traffic.md"}
 
 
 def measured_traffic(workload):
@@ -906,7 +906,7 @@ def main():
     if not args.no_cpu_baseline:
         # about 10-30 s of CPU work: all tokens of the small workloads, a
         # prefix of the large ones
-        sample = {1: 16, 2: 32, 3: 1024, 4: 256, 5: 2048, 6: 256}.get(args.workload, 32)
+        sample = {1: 16, 2: 32, 3: 4096, 4: 512, 5: 8192, 6: 512}.get(args.workload, 32)
         log(f"CPU oracle on {min(sample, T)} tokens, then the tiny and decode layers on one thread")
         res["cpu_baseline"] = cpu_baseline(d, min(sample, T))
     print(json.dumps(res), flush=True)
