@@ -923,25 +923,24 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
     for (int f = 0; f < FN; ++f)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
-  // fragment byte offsets inside a ring slot, per k16 step kk
+  // Fragment byte offsets inside a ring slot, per k16 step kk, of the wave's
+  // first A and first B fragment. Fragment i of A lies i * AFS bytes further
+  // (its rows (i*WM + wm)*32 + r32 differ from the first's by a multiple of
+  // 32, which leaves the swizzle bits, 1..3 of the row, unchanged) and
+  // fragment f of B f * BFS further (16-row blocks 2f on), so the other
+  // fragments' offsets are instruction immediates, not registers.
   const int r32 = lane & 31;
   const int khalf = lane >> 5;
-  uint32_t aoff[FM][BK / 16], boff[FN][BK / 16];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int r = (i * WM + wm) * 32 + r32;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk)
-      aoff[i][kk] = r * ROWB + (((kk * 2 + khalf) ^ ((r >> 1) & (CPR - 1))) * 16);
-  }
-#pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    const int br = wn * TN + f * 32 + r32;  // tile row of B
-    const int tb = br >> 4, rr = br & 15;
+  constexpr uint32_t AFS = WM * 32 * ROWB, BFS = 2 * KBS * 1024;
+  uint32_t aoff[BK / 16], boff[BK / 16];
+  {
+    const int r = wm * 32 + r32;
+    const int tb = (wn * TN + r32) >> 4, rr = r32 & 15;  // B: tile row wn*TN + r32
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
+      aoff[kk] = r * ROWB + (((kk * 2 + khalf) ^ ((r >> 1) & (CPR - 1))) * 16);
       const int kb = kk >> 1, c = (kk & 1) * 2 + khalf;
-      boff[f][kk] = BM * ROWB + (tb * KBS + kb) * 1024 + (c * 16 + rr) * 16;
+      boff[kk] = BM * ROWB + (tb * KBS + kb) * 1024 + (c * 16 + rr) * 16;
     }
   }
   // MFMA operands of one 16-wide k step, double-buffered across steps. Only
@@ -953,9 +952,11 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
     constexpr int NVA = decltype(nva_c)::value;
     const unsigned char* sb = ring + slot * STAGE;
 #pragma unroll
-    for (int i = 0; i < NVA; ++i) fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(sb + aoff[i][kk]);
+    for (int i = 0; i < NVA; ++i)
+      fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(sb + aoff[kk] + i * AFS);
 #pragma unroll
-    for (int f = 0; f < FN; ++f) fb[buf][f] = *reinterpret_cast<const bf16x8_t*>(sb + boff[f][kk]);
+    for (int f = 0; f < FN; ++f)
+      fb[buf][f] = *reinterpret_cast<const bf16x8_t*>(sb + boff[kk] + f * BFS);
   };
   auto mfma_step = [&](auto nva_c, int buf) {
     constexpr int NVA = decltype(nva_c)::value;
