@@ -834,7 +834,10 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
     }
   }
   __syncthreads();
-  const int e = tile_info[0], row0 = tile_info[1], rows = tile_info[2], nb = tile_info[3];
+  const int e = __builtin_amdgcn_readfirstlane(tile_info[0]);
+  const int row0 = __builtin_amdgcn_readfirstlane(tile_info[1]);
+  const int rows = __builtin_amdgcn_readfirstlane(tile_info[2]);
+  const int nb = __builtin_amdgcn_readfirstlane(tile_info[3]);
   if (rows <= 0) return;
   const int n0 = nb * OUT_COLS;
   for (int rr = tid; rr < BM; rr += NT) {
@@ -856,24 +859,36 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   const i32x4_t rsrc_a = raw_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
   const i32x4_t rsrc_b =
       raw_rsrc(reinterpret_cast<const unsigned char*>(g.B) + (size_t)e * g.b_bytes, g.b_bytes);
-  // A: load j of this wave fills tile rows [RPL*(wave*IPW + j), +RPL) of a
-  // ring slot: lane l writes slot (l%CPR) of row l/CPR, i.e. logical chunk
-  // (l%CPR) ^ swz(row). B (packed weights): each 1 KiB load copies one packed
-  // block; B load b holds tile rows [16 (b / KBS), +16) at k block b % KBS.
+  // Producer waves: the first NW/2 waves (one per SIMD: wave w runs on SIMD
+  // w mod 4) issue every direct load of a stage and the other NW/2 none, so
+  // that on each SIMD one wave keeps issuing MFMAs while the other waits for
+  // load issue slots (skewed gate-up 1,615-1,631 -> 1,579-1,592 us, down
+  // -1 %). A: producer load j fills tile rows [RPL*(j*NPW + wave), +RPL) of a
+  // ring slot; lane l writes slot (l%CPR) of row l/CPR, i.e. logical chunk
+  // (l%CPR) ^ swz(row). B (packed weights): producer load jb copies packed
+  // block jb*NPW + wave, tile rows [16 (b / KBS), +16) at k block b % KBS;
+  // its offset is uniform, so it goes in the SGPR offset and every lane's
+  // VGPR offset is just 16 * lane.
   constexpr int KBS = BK / 32;  // packed k blocks per stage
-  uint32_t voff[IPW];
-  int chunk[IPW];
-  static_assert((BM / RPL) % NW == 0, "A loads split evenly over the waves");
+  constexpr int NPW = NW / 2;
+  constexpr int APP = (BM / RPL) / NPW;             // A loads per producer
+  constexpr int BPP = (BN * 2 * BK / 1024) / NPW;   // B loads per producer
+  constexpr int IPP = APP + BPP;
+  static_assert((BM / RPL) % NPW == 0 && (BN * 2 * BK / 1024) % NPW == 0, "producer loads");
+  uint32_t vA[APP];
+  uint32_t sB[BPP];
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+  if (wave < NPW) {
 #pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int blk = j * NW + wave;
-    if (j * NW * RPL < BM) {
+    for (int j = 0; j < APP; ++j) {
+      const int blk = j * NPW + wave;
       const int r = blk * RPL + lane / CPR;
       const int c = (lane % CPR) ^ ((r >> 1) & (CPR - 1));
-      voff[j] = ((r < rows) ? a_row_off(g, row0 + r) : kOob) + c * 16;
-      chunk[j] = c * 8;
-    } else {
-      const int bl = blk - BM / RPL;
+      vA[j] = ((r < rows) ? a_row_off(g, row0 + r) : kOob) + c * 16;
+    }
+#pragma unroll
+    for (int jb = 0; jb < BPP; ++jb) {
+      const int bl = jb * NPW + wave;
       const int tb = bl / KBS, kb = bl % KBS;
       const int br = tb * 16;  // first tile row of the block
       int cb, f = 0;
@@ -885,36 +900,47 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
         cb = (n0 + br) / 16;
       }
       const uint32_t o = b_block_off<EPI>(g, cb, f);
-      voff[j] = (o == kOob) ? kOob : o + (uint32_t)kb * kb_stride<EPI>() + lane * 16;
-      chunk[j] = kb * 32 + (lane >> 4) * 8;
+      sB[jb] = __builtin_amdgcn_readfirstlane((o == kOob) ? kOob : o + (uint32_t)kb * kb_stride<EPI>());
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < APP; ++j) vA[j] = kOob;
+#pragma unroll
+    for (int jb = 0; jb < BPP; ++jb) sB[jb] = kOob;
   }
   const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_addr(ring));
   const uint32_t wave_lds = ring_base + (uint32_t)wave * 1024u;
-  auto issue = [&](int slot, int k0) {
+  // always inlined: an outlined copy would take its captures through memory
+  // and could not hand the descriptors to the loads in SGPRs
+  auto issue = [&](int slot, int k0) __attribute__((always_inline)) {
+    if (wave >= NPW) return;
     const uint32_t soff_a = (uint32_t)k0 * 2u;
     const uint32_t soff_b = (uint32_t)(k0 / 32) * kb_stride<EPI>();
     const uint32_t base = wave_lds + (uint32_t)slot * STAGE;
     if (k0 + BK <= g.kdim) {
 #pragma unroll
-      for (int j = 0; j < IPW; ++j) {
-        if (j * NW * RPL < BM)
-          dma16(rsrc_a, base + j * NW * 1024, voff[j], soff_a);
-        else
-          dma16(rsrc_b, base + j * NW * 1024, voff[j], soff_b);
-      }
+      for (int j = 0; j < APP; ++j) dma16(rsrc_a, base + j * NPW * 1024, vA[j], soff_a);
+#pragma unroll
+      for (int jb = 0; jb < BPP; ++jb)
+        dma16(rsrc_b, base + (BM / RPL + jb * NPW) * 1024, sB[jb] == kOob ? kOob : lane16,
+              __builtin_amdgcn_readfirstlane(sB[jb] == kOob ? 0u : sB[jb] + soff_b));
     } else {  // the k tail: chunks at or past kdim read as zero
 #pragma unroll
-      for (int j = 0; j < IPW; ++j) {
-        const uint32_t vo = (k0 + chunk[j] < g.kdim) ? voff[j] : kOob;
-        if (j * NW * RPL < BM)
-          dma16(rsrc_a, base + j * NW * 1024, vo, soff_a);
-        else
-          dma16(rsrc_b, base + j * NW * 1024, vo, soff_b);
+      for (int j = 0; j < APP; ++j) {
+        const int blk = j * NPW + wave;
+        const int r = blk * RPL + lane / CPR;
+        const int ck = ((lane % CPR) ^ ((r >> 1) & (CPR - 1))) * 8;
+        dma16(rsrc_a, base + j * NPW * 1024, (k0 + ck < g.kdim) ? vA[j] : kOob, soff_a);
+      }
+#pragma unroll
+      for (int jb = 0; jb < BPP; ++jb) {
+        const int kb = (jb * NPW + wave) % KBS;
+        const int ck = kb * 32 + (lane >> 4) * 8;
+        const uint32_t vo = (sB[jb] == kOob || k0 + ck >= g.kdim) ? kOob : sB[jb] + lane16;
+        dma16(rsrc_b, base + (BM / RPL + jb * NPW) * 1024, vo, soff_b);
       }
     }
   };
-
   const int wm = wave % WM, wn = wave / WM;
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -978,7 +1004,10 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
     __syncthreads();  // row tables written; ring free
 #pragma unroll
     for (int st = 0; st < NS; ++st) issue(st, st * BK);
-    wait_barrier<(NS - 1) * IPW>();  // stage 0 landed (every wave's loads)
+    if (wave < NPW)
+      wait_barrier<(NS - 1) * IPP>();  // stage 0 landed (every producer's loads)
+    else
+      wait_barrier<0>();
     if (NVA > 0) read_step(nva_c, 0, 0, 0);
     int cur = 0;
     for (int kt = 0; kt < nk; ++kt) {
@@ -993,7 +1022,8 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
           // the barrier), and every wave has finished its LDS reads of stage
           // kt (lgkmcnt(0) before the barrier), so its slot takes stage
           // kt+NS.
-          wait_barrier<(NS - 2) * IPW>();
+          static_assert(NS == 2, "per-stage wait for two ring slots");
+          wait_barrier<0>();
           issue(cur, (kt + NS) * BK);
           if (NVA > 0) read_step(nva_c, b ^ 1, nxt, 0);
         }
