@@ -312,3 +312,42 @@ def test_tiled_gateup_tail_tiles_bit_exact(gpu_lib, bm, tails, full, I):
                                                to_dev(off), K)
     torch.cuda.synchronize()
     assert_bits_equal(bits(act), O.gateup_silu(x, wgu, sp, off, K), "act")
+
+
+def _bf16_nan(b):
+    b = np.asarray(b, np.uint16)
+    return ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+
+
+def test_tiled_gateup_silu_every_bf16_gate(gpu_lib):
+    """SiLU-mul of the 320 x 256 tile kernel for every bf16 gate value.
+
+    One-hot activation rows (row p has 1 at k = p mod 32) pick gate value
+    W_g[c, p mod 32] and up value 1, so the 32 distinct rows x 2,048 columns
+    hold all 65,536 bf16 bit patterns as the gate (the 65,280 finite ones in
+    columns 0..2039; the infinities and NaNs in 2040..2047, where 0 * inf
+    makes every gate NaN). 10,240 rows put the call on the 320-row tiles.
+    Bit-exact against the oracle, NaNs by position.
+    """
+    P, H, I = 10240, 32, 2048
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    special = ((pats & 0x7F80) == 0x7F80)
+    order = np.concatenate([pats[~special], pats[special]])
+    assert order.size == I * H and int((~special).sum()) == (I - 8) * H
+    wgu = np.empty((1, 2 * I, H), np.uint16)
+    wgu[0, :I] = order.reshape(I, H)
+    wgu[0, I:] = O.bf16_from_f32(np.ones((I, H), F32))
+    x = np.zeros((P, H), np.uint16)
+    x[np.arange(P), np.arange(P) % H] = O.bf16_from_f32(np.ones(1, F32))[0]
+    act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), packed_gu(wgu), None, None, 1)
+    torch.cuda.synchronize()
+    got = bits(act)
+    ref = O.gateup_silu(x[:H], wgu, None, None, 1)
+    gn, rn = _bf16_nan(got[:H]), _bf16_nan(ref)
+    assert np.array_equal(gn, rn), f"NaN positions differ: {int((gn != rn).sum())}"
+    assert rn[:, I - 8:].all() and not rn[:, :I - 8].all()
+    diff = int(np.count_nonzero(np.where(gn, 0, got[:H]) != np.where(rn, 0, ref)))
+    assert diff == 0, f"{diff} of {ref.size} act values differ"
+    # every row repeats the row of its one-hot position
+    rep = got.reshape(P // H, H, I)
+    assert np.array_equal(rep, np.broadcast_to(got[:H], rep.shape))
