@@ -1213,16 +1213,19 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
                          : run(stream_kernel<EPI, 1, 1, 3, 4>, grid_for(g), 192, s, g);
       }
       // tens of rows per tile: 32-row tiles; gate-up 32 columns with k over
-      // 8 waves (routed) or 4 (dense), down 64 columns with k over 2 waves
-      // (measured at 16 rows per expert: 256 experts, 512 tokens, top-8)
+      // 4 waves, down 64 columns with k in one wave for routed rows (2 for a
+      // dense expert), measured at 16 rows per expert (256 experts, 512
+      // tokens, top-8): against 8 and 2 k-waves, gate-up 190 -> 184 us and
+      // down 112 -> 108 us; 16-row tiles, 64- or 128-column gate-up blocks
+      // and 128-column down blocks measured slower
       g.slots = slots_for(g.P, g.E, 32, grouped);
       if constexpr (EPI == EPI_GATEUP) {
         g.nblk = (g.n_out + 31) / 32;
-        if (grouped) return run(stream_kernel<EPI, 2, 2, 8, 4, true>, grid_for(g), 512, s, g);
+        if (grouped) return run(stream_kernel<EPI, 2, 2, 4, 4, true>, grid_for(g), 256, s, g);
         return run(stream_kernel<EPI, 2, 2, 4, 4>, grid_for(g), 256, s, g);
       } else {
         g.nblk = (g.n_out + 63) / 64;
-        return grouped ? run(stream_kernel<EPI, 2, 4, 2, 4, true>, grid_for(g), 128, s, g)
+        return grouped ? run(stream_kernel<EPI, 2, 4, 1, 4, true>, grid_for(g), 64, s, g)
                        : run(stream_kernel<EPI, 2, 4, 2, 4>, grid_for(g), 128, s, g);
       }
     } else if constexpr (EPI == EPI_GATEUP) {
