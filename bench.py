@@ -104,11 +104,11 @@ def algorithmic_work(cfg, offsets):
     return gu, dn, touched
 
 
-KERNEL_CODE_FILES = ("gemm.hip", "device_math.h", "lds_dma.h")
+KERNEL_CODE_FILES = ("gemm.hip", "device_math.h", "lds_dma.h", "silu_table.h")
 
 
 def kernel_code_fingerprint():
-    """sha256 of the GEMM kernel code (gemm.hip, device_math.h, lds_dma.h) with
+    """sha256 of the GEMM kernel code (gemm.hip and its headers) with
     comments and whitespace removed: it changes when the code changes, not
     when a comment does."""
     import hashlib

@@ -38,17 +38,15 @@ __device__ __forceinline__ float round_bf16(float f) {
   return bf16_to_f32(f32_to_bf16(f));
 }
 
-// Two f32 values rounded to bf16 (nearest even) by one v_cvt_pk_bf16_f32 and
-// read back as f32: lo and hi. For a NaN input the result is a NaN whose
-// payload is the hardware's (the narrowing of the gate-up pair, N1, where
-// only the NaN-ness of a NaN can matter).
-__device__ __forceinline__ void round_bf16_pair(float& lo, float& hi) {
+// Two f32 values rounded to bf16 (nearest even) by one v_cvt_pk_bf16_f32:
+// lo in the low half, hi in the high half. For a NaN input the half is a NaN
+// whose payload is the hardware's (the narrowing of the gate-up pair, N1,
+// where only the NaN-ness of a NaN can matter).
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));
   const f32x2_t v = {lo, hi};
-  const uint32_t p = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b16x2_t));
-  lo = __uint_as_float(p << 16);
-  hi = __uint_as_float(p & 0xFFFF0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b16x2_t));
 }
 
 // e^x in f32: Cody & Waite argument reduction (n = rint(x / ln2),

@@ -51,8 +51,13 @@
 #include "device_math.h"
 #include "launch.h"
 #include "lds_dma.h"
+#include "silu_table.h"
 
 namespace moe {
+
+// silu_cw of the 7,936 bf16 gate values without a closed form (silu_table.h),
+// built by the compiler; 32 KiB of read-only device memory.
+__constant__ SiluTable kSiluTable = make_silu_table();
 
 enum { EPI_GATEUP = 0, EPI_DOWN = 1, EPI_F32 = 2 };
 
@@ -807,6 +812,15 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   // the bf16 output tile goes through the ring in NP passes of BM / NP rows
   constexpr int NP = (BM * CLD * 2 <= NS * STAGE) ? 1 : 2;
   static_assert((BM / NP) * CLD * 2 <= NS * STAGE && BM % (32 * NP) == 0, "output staging");
+  // Gate-up: the one stage issued past the end of k brings the SiLU table
+  // (silu_table.h) into its ring slot instead of zeros, into the first 32 KiB
+  // of slot 0 or the last 32 KiB of slot 1; the output staging then takes the
+  // other end of the ring.
+  constexpr bool TAB = EPI == EPI_GATEUP;
+  static_assert(!TAB || (NS == 2 && NP == 1 && STAGE >= kSiluTabBytes &&
+                         BM * CLD * 2 + kSiluTabBytes <= NS * STAGE &&
+                         (NS * STAGE - BM * CLD * 2) % 16 == 0 && kSiluTabBytes % (1024 * NW / 2) == 0),
+                "SiLU table space");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE];
   __shared__ int row_dest[BM];
   __shared__ float row_w[BM];
@@ -921,10 +935,22 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   }
   const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_addr(ring));
   const uint32_t wave_lds = ring_base + (uint32_t)wave * 1024u;
+  const i32x4_t rsrc_t = raw_rsrc(&kSiluTable, kSiluTabBytes);
   // always inlined: an outlined copy would take its captures through memory
   // and could not hand the descriptors to the loads in SGPRs
   auto issue = [&](int slot, int k0) __attribute__((always_inline)) {
     if (wave >= NPW) return;
+    if constexpr (TAB) {
+      if (k0 >= g.kdim) {  // past the end of k: the SiLU table, 1 KiB per load
+        const uint32_t tb = ring_base + (slot == 0 ? 0u : (uint32_t)(NS * STAGE - kSiluTabBytes));
+#pragma unroll
+        for (int j = 0; j < kSiluTabBytes / 1024 / NPW; ++j) {
+          const uint32_t blk = (uint32_t)(j * NPW + wave) * 1024u;
+          dma16(rsrc_t, tb + blk, lane16, blk);
+        }
+        return;
+      }
+    }
     const uint32_t soff_a = (uint32_t)k0 * 2u;
     const uint32_t soff_b = (uint32_t)(k0 / 32) * kb_stride<EPI>();
     const uint32_t base = wave_lds + (uint32_t)slot * STAGE;
@@ -1015,10 +1041,10 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
     __syncthreads();  // row tables written; ring free
 #pragma unroll
     for (int st = 0; st < NS; ++st) issue(st, st * BK);
-    if (wave < NPW)
+    if (wave < NPW && !(TAB && nk < 2))
       wait_barrier<(NS - 1) * IPP>();  // stage 0 landed (every producer's loads)
     else
-      wait_barrier<0>();
+      wait_barrier<0>();  // (with the table as stage 1, every load)
     if (NVA > 0) read_step(nva_c, 0, 0, 0);
     int cur = 0;
     for (int kt = 0; kt < nk; ++kt) {
@@ -1065,11 +1091,15 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
     case 4: if constexpr (FM >= 4) main_loop(std::integral_constant<int, 4>{}); break;
     default: if constexpr (FM >= 5) main_loop(std::integral_constant<int, FM>{}); break;
   }
-  wait_barrier<0>();  // ring free for the output staging
+  wait_barrier<0>();  // ring free for the output staging; the table landed
 
   // Epilogue (as in tiled_kernel): bf16 results into LDS, then 16-byte row
-  // segments to the output rows, in NP passes of PR rows.
-  uint16_t* smem = reinterpret_cast<uint16_t*>(ring);
+  // segments to the output rows, in NP passes of PR rows. The table's slot is
+  // that of stage max(nk, 1), the last one issued.
+  const bool tab0 = ((nk >= 2 ? nk : 1) & 1) == 0;
+  uint16_t* smem =
+      reinterpret_cast<uint16_t*>(ring + ((TAB && tab0) ? NS * STAGE - BM * CLD * 2 : 0));
+  const float* tab = reinterpret_cast<const float*>(ring + (tab0 ? 0 : NS * STAGE - kSiluTabBytes));
   constexpr int PR = BM / NP;
 #pragma unroll
   for (int pass = 0; pass < NP; ++pass) {
@@ -1086,9 +1116,11 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
 #pragma unroll
         for (int pp = 0; pp < FN / 2; ++pp) {
 #pragma clang fp contract(off)
-          float gb = acc[i][2 * pp][r], ub = acc[i][2 * pp + 1][r];
-          round_bf16_pair(gb, ub);  // N1: narrow before the activation
-          crow[wn * (TN / 2) + pp * 32 + r32] = (uint16_t)f32_to_bf16(silu_cw(gb) * ub);
+          // N1: gate and up narrowed to bf16 before the activation
+          const uint32_t gu = bf16x2_bits(acc[i][2 * pp][r], acc[i][2 * pp + 1][r]);
+          const float ub = __uint_as_float(gu & 0xFFFF0000u);
+          crow[wn * (TN / 2) + pp * 32 + r32] =
+              (uint16_t)f32_to_bf16(silu_bf16(gu & 0xFFFFu, tab) * ub);
         }
       } else {
         const float w = row_w[rr];
