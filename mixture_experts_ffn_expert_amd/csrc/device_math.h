@@ -21,16 +21,13 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// f32 -> bf16 bits, round to nearest even: the conversion the compiler emits
-// for a float -> __bf16 cast on gfx950 (v_cvt_pk_bf16_f32, IEEE round to
-// nearest even, subnormals kept, values past the largest bf16 to infinity).
-// A NaN keeps its sign and top payload bits and gets the quiet bit, selected
-// without a branch.
+// f32 -> bf16 bits: the hardware conversion the compiler emits for a float ->
+// __bf16 cast on gfx950 (v_cvt_pk_bf16_f32). On every one of the 2^32 f32
+// patterns it rounds to nearest even, keeps subnormals, takes values past the
+// largest bf16 to infinity, and turns a NaN into sign and top payload bits
+// with the quiet bit set, i.e. (bits >> 16) | 0x0040.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rn = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
-  const uint32_t qn = (u >> 16) | 0x0040u;
-  return (f != f) ? qn : rn;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // f32 rounded to bf16 and read back as f32 (one narrowing).
@@ -38,10 +35,8 @@ __device__ __forceinline__ float round_bf16(float f) {
   return bf16_to_f32(f32_to_bf16(f));
 }
 
-// Two f32 values rounded to bf16 (nearest even) by one v_cvt_pk_bf16_f32:
-// lo in the low half, hi in the high half. For a NaN input the half is a NaN
-// whose payload is the hardware's (the narrowing of the gate-up pair, N1,
-// where only the NaN-ness of a NaN can matter).
+// Two f32 values converted to bf16 (as f32_to_bf16) by one
+// v_cvt_pk_bf16_f32: lo in the low half, hi in the high half.
 __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 b16x2_t __attribute__((ext_vector_type(2)));

@@ -1108,8 +1108,10 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   for (int i = 0; i < FM; ++i) {
     if (((i * WM + wm) * 32) / PR != pass) continue;  // fragment rows lie in one pass
     if (i >= nva) continue;  // wholly past the tile's last row: nothing to store
+    // accumulator entries r and r + 1 of a lane are rows rr and rr + 1 of one
+    // column: each pair becomes bf16 in one conversion
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 16; r += 2) {
       const int rr = (i * WM + wm) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
       uint16_t* crow = smem + (rr - pass * PR) * CLD;
       if (EPI == EPI_GATEUP) {
@@ -1117,19 +1119,24 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
         for (int pp = 0; pp < FN / 2; ++pp) {
 #pragma clang fp contract(off)
           // N1: gate and up narrowed to bf16 before the activation
-          const uint32_t gu = bf16x2_bits(acc[i][2 * pp][r], acc[i][2 * pp + 1][r]);
-          const float ub = __uint_as_float(gu & 0xFFFF0000u);
-          crow[wn * (TN / 2) + pp * 32 + r32] =
-              (uint16_t)f32_to_bf16(silu_bf16(gu & 0xFFFFu, tab) * ub);
+          const uint32_t gu0 = bf16x2_bits(acc[i][2 * pp][r], acc[i][2 * pp + 1][r]);
+          const uint32_t gu1 = bf16x2_bits(acc[i][2 * pp][r + 1], acc[i][2 * pp + 1][r + 1]);
+          const float y0 = silu_bf16(gu0 & 0xFFFFu, tab) * __uint_as_float(gu0 & 0xFFFF0000u);
+          const float y1 = silu_bf16(gu1 & 0xFFFFu, tab) * __uint_as_float(gu1 & 0xFFFF0000u);
+          const uint32_t o = bf16x2_bits(y0, y1);
+          crow[wn * (TN / 2) + pp * 32 + r32] = (uint16_t)o;
+          crow[CLD + wn * (TN / 2) + pp * 32 + r32] = (uint16_t)(o >> 16);
         }
       } else {
-        const float w = row_w[rr];
+        // N2: the weight on the accumulator (row_w is 1 without weights, and
+        // y * 1 is y)
+        const float w0 = row_w[rr], w1 = row_w[rr + 1];
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
 #pragma clang fp contract(off)
-          float y = acc[i][f][r];
-          if (g.pair_w != nullptr) y = y * w;  // N2: weight on the accumulator
-          crow[wn * TN + f * 32 + r32] = (uint16_t)f32_to_bf16(y);
+          const uint32_t o = bf16x2_bits(acc[i][f][r] * w0, acc[i][f][r + 1] * w1);
+          crow[wn * TN + f * 32 + r32] = (uint16_t)o;
+          crow[CLD + wn * TN + f * 32 + r32] = (uint16_t)(o >> 16);
         }
       }
     }

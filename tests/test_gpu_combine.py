@@ -116,8 +116,9 @@ def test_bf16_store_rounding_sweep(gpu_lib):
     step up, just below / at / just above the tie, the largest, and two
     random), which covers ties to even, subnormals, the carry into the
     exponent, overflow to infinity and NaN. K = 1, unweighted, scale 1, no
-    shared term: out = bf16(+0 + v). NaN outputs compare by position and
-    sign (the payload of an add's NaN result is the hardware's choice)."""
+    shared term: out = bf16(+0 + v). Every output bit is compared, NaNs
+    included: the add keeps a quiet NaN's payload, and the conversion keeps
+    sign and top payload bits and sets the quiet bit, as the oracle does."""
     g = np.random.Generator(np.random.PCG64(77))
     hi = np.arange(1 << 16, dtype=np.uint32) << 16
     lows = [0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF]
@@ -132,12 +133,7 @@ def test_bf16_store_rounding_sweep(gpu_lib):
     got = bits(out).astype(np.uint32)
     ref = O.combine_gate(v, T, 1, H, None, 1.0, None, None, eo_bf16=False, out_bf16=True)
     ref = ref.astype(np.uint32)
-    nan_g = (got & 0x7F80) == 0x7F80
-    nan_g &= (got & 0x7F) != 0
     nan_r = ((ref & 0x7F80) == 0x7F80) & ((ref & 0x7F) != 0)
-    assert np.array_equal(nan_g, nan_r), "NaN positions differ"
-    assert np.array_equal(got[nan_g] & 0x8000, ref[nan_r] & 0x8000), "NaN signs differ"
-    ok = ~nan_r
-    diff = int(np.count_nonzero(got[ok] != ref[ok]))
-    assert diff == 0, f"{diff} of {int(ok.sum())} non-NaN stores differ"
-    assert int(ok.sum()) > 500000
+    diff = int(np.count_nonzero(got != ref))
+    assert diff == 0, f"{diff} of {got.size} stores differ"
+    assert int(nan_r.sum()) > 2000 and int((~nan_r).sum()) > 500000
