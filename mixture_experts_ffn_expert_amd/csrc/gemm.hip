@@ -804,7 +804,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   constexpr int OUT_COLS = (EPI == EPI_GATEUP) ? BN / 2 : BN;
   constexpr int CLD = OUT_COLS + 8;            // output staging row (elements)
   static_assert(BK == 64 || BK == 32, "k step");
-  static_assert(NS >= 2 && (NS - 2) * IPW <= 63, "ring depth (vmcnt range)");
+  static_assert(NS == 2, "two ring slots");
   static_assert(IPW * RPL * NW == BM + BN, "loads per wave");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "swizzle period");
   static_assert(EPI != EPI_GATEUP || FN % 2 == 0, "gate-up pairs fragments");
@@ -824,6 +824,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE];
   __shared__ int row_dest[BM];
   __shared__ float row_w[BM];
+  __shared__ uint32_t row_a[BM];  // byte offset of each tile row's A row (kOob: none)
   __shared__ int tile_info[4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -865,9 +866,14 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   const int nb = __builtin_amdgcn_readfirstlane(tile_info[3]);
   if (rows <= 0) return;
   const int n0 = nb * OUT_COLS;
+  // Row tables, one tile row per thread: output row and weight for the
+  // epilogue, and the A row offset that the producers' loads use (for the
+  // gate-up a gather through the sorted pairs: one load per row here instead
+  // of one per row and producer lane).
   for (int rr = tid; rr < BM; rr += NT) {
     int dest = -1;
     float wgt = 1.0f;
+    uint32_t ao = kOob;
     if (rr < rows) {
       const int q = row0 + rr;
       dest = q;
@@ -876,10 +882,13 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
         if (dest < 0 || dest >= g.P) dest = -1;
       }
       if (EPI == EPI_DOWN && g.pair_w != nullptr && dest >= 0) wgt = g.pair_w[dest];
+      ao = a_row_off(g, q);
     }
     row_dest[rr] = dest;
     row_w[rr] = wgt;
+    row_a[rr] = ao;
   }
+  __syncthreads();
 
   const i32x4_t rsrc_a = raw_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
   const i32x4_t rsrc_b =
@@ -898,7 +907,6 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   constexpr int NPW = NW / 2;
   constexpr int APP = (BM / RPL) / NPW;             // A loads per producer
   constexpr int BPP = (BN * 2 * BK / 1024) / NPW;   // B loads per producer
-  constexpr int IPP = APP + BPP;
   static_assert((BM / RPL) % NPW == 0 && (BN * 2 * BK / 1024) % NPW == 0, "producer loads");
   uint32_t vA[APP];
   uint32_t sB[BPP];
@@ -909,7 +917,7 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
       const int blk = j * NPW + wave;
       const int r = blk * RPL + lane / CPR;
       const int c = (lane % CPR) ^ ((r >> 1) & (CPR - 1));
-      vA[j] = ((r < rows) ? a_row_off(g, row0 + r) : kOob) + c * 16;
+      vA[j] = row_a[r] + c * 16;
     }
 #pragma unroll
     for (int jb = 0; jb < BPP; ++jb) {
@@ -1032,20 +1040,19 @@ __global__ __launch_bounds__(64 * WM * WN) void tiled_dma_kernel(GemmArgs g) {
   };
 
   const int nk = (g.kdim + BK - 1) / BK;
-  // The ring holds stages kt .. kt+NS-1 while stage kt is multiplied. Every
-  // wave issues IPW loads per stage, also for stages past the end of k (they
-  // read nothing and write zeros into a free slot), so that "stage kt+1 has
-  // landed" is always vmcnt((NS - 2) * IPW).
+  // The ring holds stages kt and kt+1 while stage kt is multiplied; each
+  // stage ends with vmcnt(0) and a barrier, after which stage kt+2 goes into
+  // the slot just read. The one stage issued past the end of k loads the
+  // SiLU table into its free slot (gate-up) or zeros (down).
   auto main_loop = [&](auto nva_c) {
     constexpr int NVA = decltype(nva_c)::value;
-    __syncthreads();  // row tables written; ring free
-#pragma unroll
-    for (int st = 0; st < NS; ++st) issue(st, st * BK);
-    if (wave < NPW && !(TAB && nk < 2))
-      wait_barrier<(NS - 1) * IPP>();  // stage 0 landed (every producer's loads)
-    else
-      wait_barrier<0>();  // (with the table as stage 1, every load)
+    // Stage 0 goes out alone and is waited for; stage 1 (or the SiLU table)
+    // is issued once the first k step's operands are being read, so that the
+    // producers' issue of it overlaps the other waves' first MFMAs.
+    issue(0, 0);
+    wait_barrier<0>();
     if (NVA > 0) read_step(nva_c, 0, 0, 0);
+    issue(1, BK);
     int cur = 0;
     for (int kt = 0; kt < nk; ++kt) {
       const int nxt = (cur + 1 == NS) ? 0 : cur + 1;
