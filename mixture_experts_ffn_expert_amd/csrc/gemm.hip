@@ -1226,19 +1226,20 @@ static hipError_t dispatch(GemmArgs g, hipStream_t s) {
       g.slots = slots_for(g.P, g.E, 16, false);
       return run(stream_kernel<EPI, 1, 1, 8, 4>, grid_for(g), 512, s, g);
     }
-    // many tokens (shapes from a sweep of nine at 512, 4096 and 8192 tokens):
-    // up to 1024 tokens 32 rows x 32 columns with k over 8 waves; from 8192
-    // tokens 64 rows x 64 columns with k over 4 waves; between them 32 rows x
-    // 64 columns with k over 4 waves
+    // many tokens (shapes from sweeps at 512, 4096 and 8192 tokens): up to
+    // 1024 tokens 16 rows x 32 columns with k over 8 waves (512 x 2048 x 256:
+    // 9.9 -> 7.8 us against 32 x 32); from 8192 tokens 64 rows x 64 columns
+    // with k over 8 waves (8192 x 4096 x 128: 39.8 -> 36.5 us against 4
+    // waves); between them 32 rows x 64 columns with k over 4 waves
     if (g.P <= 1024) {
       g.nblk = (g.n_out + 31) / 32;
-      g.slots = slots_for(g.P, g.E, 32, false);
-      return run(stream_kernel<EPI, 2, 2, 8, 4>, grid_for(g), 512, s, g);
+      g.slots = slots_for(g.P, g.E, 16, false);
+      return run(stream_kernel<EPI, 1, 2, 8, 4>, grid_for(g), 512, s, g);
     }
     if (g.P >= 8192) {
       g.nblk = (g.n_out + 63) / 64;
       g.slots = slots_for(g.P, g.E, 64, false);
-      return run(stream_kernel<EPI, 4, 4, 4, 2>, grid_for(g), 256, s, g);
+      return run(stream_kernel<EPI, 4, 4, 8, 2>, grid_for(g), 512, s, g);
     }
     g.nblk = (g.n_out + 63) / 64;
     g.slots = slots_for(g.P, g.E, 32, false);
