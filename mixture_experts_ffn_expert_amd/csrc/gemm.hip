@@ -378,8 +378,26 @@ __device__ __forceinline__ bool stream_body(const GemmArgs& g, int blk, float* r
   if (!find_tile(g, BM, slot, e, row0, rows)) return false;  // uniform over the workgroup
   const int col0 = nb * 16 * NFO;
 
+  // MFMA lane order of an operand: lane l holds row l % 16, k chunk l / 16
   const int r16 = lane & 15;
   const int kc = (lane >> 4) * 8;
+  // Plain-row operands (both sides of the logits) are loaded coalesced
+  // instead: four consecutive lanes read one row's 64 bytes (row l / 4,
+  // chunk l % 4), and a lane permutation puts them in MFMA order. Loaded in
+  // MFMA order, the 64 lanes of a load touch 64 separate 16-byte pieces.
+  constexpr bool PACKED = EPI != EPI_F32;
+  const int lr16 = PACKED ? r16 : (lane >> 2);
+  const int lkc = PACKED ? kc : (lane & 3) * 8;
+  const int perm_src = (4 * (lane & 15) + (lane >> 4)) * 4;  // ds_bpermute byte index
+  auto to_mfma = [&](bf16x8_t v) -> bf16x8_t {
+    if constexpr (PACKED) return v;
+    u32x4_t u = __builtin_bit_cast(u32x4_t, v);
+    u.x = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_src, (int)u.x);
+    u.y = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_src, (int)u.y);
+    u.z = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_src, (int)u.z);
+    u.w = (uint32_t)__builtin_amdgcn_ds_bpermute(perm_src, (int)u.w);
+    return __builtin_bit_cast(bf16x8_t, u);
+  };
   const __amdgpu_buffer_rsrc_t ra_rsrc =
       make_rsrc(g.A, (uint32_t)g.a_rows * (uint32_t)g.kdim * 2u);
   const __amdgpu_buffer_rsrc_t rb_rsrc =
@@ -387,13 +405,12 @@ __device__ __forceinline__ bool stream_body(const GemmArgs& g, int blk, float* r
   uint32_t va[MF];
 #pragma unroll
   for (int i = 0; i < MF; ++i) {
-    const int rr = i * 16 + r16;
-    va[i] = ((rr < rows) ? a_row_off(g, row0 + rr) : kOob) + kc * 2;
+    const int rr = i * 16 + lr16;
+    va[i] = ((rr < rows) ? a_row_off(g, row0 + rr) : kOob) + lkc * 2;
   }
   // B: plain rows for the logits (k position in the scalar offset); packed
   // blocks for the expert weights, where lane l's 16 bytes of a 32-wide k
   // step are the l-th chunk of one 1 KiB block
-  constexpr bool PACKED = EPI != EPI_F32;
   uint32_t vb[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f) {
@@ -402,7 +419,7 @@ __device__ __forceinline__ bool stream_body(const GemmArgs& g, int blk, float* r
       const uint32_t o = b_block_off<EPI>(g, col0 / 16 + fo, f & 1);
       vb[f] = (o == kOob) ? kOob : o + lane * 16;
     } else {
-      vb[f] = b_row_off(g, col0 + fo * 16 + r16) + kc * 2;
+      vb[f] = b_row_off(g, col0 + fo * 16 + lr16) + lkc * 2;
     }
   }
   // scalar B offset of the 32-wide k step starting at k
@@ -454,22 +471,27 @@ __device__ __forceinline__ bool stream_body(const GemmArgs& g, int blk, float* r
         for (int i = 0; i < MF; ++i) a[u][i] = bload8(ra_rsrc, va[i], soff);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int f = 0; f < NB; ++f) b[u][f] = to_mfma(b[u][f]);
+#pragma unroll
+        for (int i = 0; i < MF; ++i) a[u][i] = to_mfma(a[u][i]);
 #pragma unroll
         for (int i = 0; i < MF; ++i)
 #pragma unroll
           for (int f = 0; f < NB; ++f)
             acc[i][f] =
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][i], b[u][f], acc[i][f], 0, 0, 0);
+      }
     }
     for (; k0 < ke; k0 += 32) {  // tail: 8-element chunks at or past ke read as zero
-      const bool in = k0 + kc < ke;
+      const bool in = k0 + lkc < ke;
       const uint32_t soff = (uint32_t)k0 * 2u;
       bf16x8_t a[MF], b[NB];
 #pragma unroll
-      for (int f = 0; f < NB; ++f) b[f] = bload8(rb_rsrc, in ? vb[f] : kOob, bsoff(k0));
+      for (int f = 0; f < NB; ++f) b[f] = to_mfma(bload8(rb_rsrc, in ? vb[f] : kOob, bsoff(k0)));
 #pragma unroll
-      for (int i = 0; i < MF; ++i) a[i] = bload8(ra_rsrc, in ? va[i] : kOob, soff);
+      for (int i = 0; i < MF; ++i) a[i] = to_mfma(bload8(ra_rsrc, in ? va[i] : kOob, soff));
 #pragma unroll
       for (int i = 0; i < MF; ++i)
 #pragma unroll
