@@ -250,6 +250,18 @@ __device__ __forceinline__ uint2 kq_load8(__amdgpu_buffer_rsrc_t r, uint32_t off
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
+// Coalesced operand loads. In the order of a v_mfma_i32_16x16x32_i8 operand
+// lane l holds row l % 16, 8-byte chunk l / 16 of a 32-value group, so a
+// load in that order has its 64 lanes read 64 separate 8-byte pieces. The
+// code bytes (activation codes; Q4_K / Q5_K nibbles and high bits) are
+// loaded with four consecutive lanes reading one row's 32 bytes (row l / 4,
+// chunk l % 4) instead, and this permutation (psrc: byte index of the
+// source lane) puts each lane's 8 bytes in MFMA order.
+__device__ __forceinline__ uint2 kq_perm8(uint2 v, int psrc) {
+  return make_uint2((uint32_t)__builtin_amdgcn_ds_bpermute(psrc, (int)v.x),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(psrc, (int)v.y));
+}
+
 __device__ __forceinline__ long kq_pair(uint32_t lo, uint32_t hi) {
   return (long)(((uint64_t)hi << 32) | lo);
 }
@@ -287,27 +299,48 @@ struct KqW<KQ_Q8_0> {
 
 // Loads the unit at byte offset `base` (kqOob-based offsets stay out of
 // range) of this lane's weight row; lane chunk kc of every 32-value group.
-template <int FMT>
+// The code bytes come coalesced from the unit at base_c of row l / 4 (chunk
+// kcc = l % 4) and are permuted into MFMA order; headers, scales and the
+// Q8_0 block scales are read for this lane's own row.
+template <int FMT, bool CO>
 __device__ __forceinline__ void kq_wload(KqW<FMT>& w, __amdgpu_buffer_rsrc_t r, uint32_t base,
-                                         int kc) {
+                                         int kc, uint32_t base_c, int kcc, int psrc) {
+  if constexpr (!CO) {  // code bytes in MFMA order, straight from this lane's row
+    base_c = base;
+    kcc = kc;
+  }
+  auto perm = [&](uint2 v) -> uint2 {
+    if constexpr (CO) return kq_perm8(v, psrc);
+    return v;
+  };
   if constexpr (FMT == KQ_Q4_K) {
     w.hdr = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, base, 0, 0));
 #pragma unroll
-    for (int p = 0; p < 4; ++p) w.qs[p] = kq_load8(r, base + 16 + p * 32 + kc * 8);
+    for (int p = 0; p < 4; ++p) w.qs[p] = kq_load8(r, base_c + 16 + p * 32 + kcc * 8);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w.qs[p] = perm(w.qs[p]);
   } else if constexpr (FMT == KQ_Q5_K) {
     w.hdr = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, base, 0, 0));
-    w.qh = kq_load8(r, base + 16 + kc * 8);
+    w.qh = kq_load8(r, base_c + 16 + kcc * 8);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) w.qs[p] = kq_load8(r, base + 48 + p * 32 + kc * 8);
+    for (int p = 0; p < 4; ++p) w.qs[p] = kq_load8(r, base_c + 48 + p * 32 + kcc * 8);
+    w.qh = perm(w.qh);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) w.qs[p] = perm(w.qs[p]);
   } else if constexpr (FMT == KQ_Q6_K) {
     // 210-byte blocks: base is 2-aligned; every load stays in [base - 2,
     // base + 210)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) w.ql[2 * h + c2] = kq_load8_a2(r, base + 64 * h + 32 * c2 + kc * 8);
+      for (int c2 = 0; c2 < 2; ++c2)
+        w.ql[2 * h + c2] = kq_load8_a2(r, base_c + 64 * h + 32 * c2 + kcc * 8);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) w.qh[h] = kq_load8_a2(r, base + 128 + 32 * h + kc * 8);
+    for (int h = 0; h < 2; ++h) w.qh[h] = kq_load8_a2(r, base_c + 128 + 32 * h + kcc * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w.ql[i] = perm(w.ql[i]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) w.qh[h] = perm(w.qh[h]);
     w.sh = base & 3u;
     w.sc = __builtin_bit_cast(i32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, base + 192 - w.sh, 0, 0));
     w.sc_tail = __builtin_amdgcn_raw_buffer_load_b16(r, base + 206, 0, 0);
@@ -317,9 +350,11 @@ __device__ __forceinline__ void kq_wload(KqW<FMT>& w, __amdgpu_buffer_rsrc_t r, 
     // the quants of even blocks sit 2 bytes past a dword boundary
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const uint32_t qo = base + 34 * b + 2 + kc * 8;
+      const uint32_t qo = base_c + 34 * b + 2 + kcc * 8;
       w.q[b] = (b & 1) ? kq_load8(r, qo) : kq_load8_a2(r, qo);
     }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) w.q[b] = perm(w.q[b]);
     // the four lanes of a row share its 8 scales: lane chunk kc loads two
     // of them, the others come by lane exchange (kq_frag)
     const uint32_t dl = __builtin_amdgcn_raw_buffer_load_b16(r, base + 68 * kc, 0, 0);
@@ -336,14 +371,25 @@ struct KqA {
   float dx[4][8];   // scales of the 4 C rows (K-quants: [i][0]; Q8_0: per block)
 };
 
-template <int FMT>
+// The activation codes come coalesced from row arow_c (chunk kcc) and are
+// permuted into MFMA order; scales and sums are read in MFMA order.
+template <int FMT, bool CO>
 __device__ __forceinline__ void kq_aload(KqA<FMT>& a, const KqArgs& g,
                                          __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rd,
                                          __amdgpu_buffer_rsrc_t rs, int arow, const int* crow,
-                                         int u, int kc) {
-  const uint32_t aq = (arow >= 0) ? (uint32_t)arow * (uint32_t)g.kdim + u * kQK + kc * 8 : kqOob;
+                                         int u, int kc, int arow_c, int kcc, int psrc) {
+  if constexpr (!CO) {
+    arow_c = arow;
+    kcc = kc;
+  }
+  const uint32_t aq =
+      (arow_c >= 0) ? (uint32_t)arow_c * (uint32_t)g.kdim + u * kQK + kcc * 8 : kqOob;
+  uint2 ac[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) a.aop[j] = (long)__builtin_bit_cast(uint64_t, kq_load8(rq, aq + j * 32));
+  for (int j = 0; j < 8; ++j) ac[j] = kq_load8(rq, aq + j * 32);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    a.aop[j] = (long)__builtin_bit_cast(uint64_t, CO ? kq_perm8(ac[j], psrc) : ac[j]);
   const int nsb = g.kdim / kQK;
   if constexpr (FMT == KQ_Q8_0) {
     // 8 f16 scales per row and unit: one 16-byte load per C row
@@ -519,6 +565,14 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
   const int col0 = nb * 16 * NFO;
   const int r16 = lane & 15;   // A row / B column of this lane's MFMA operands
   const int kc = lane >> 4;    // 8-value k chunk of a 32-value group
+  // coalesced loads (gate-up): row lane / 4, chunk lane % 4, then permuted
+  // (kq_perm8). Measured per format and GEMM: Q4_K gate-up 72 -> 62 us,
+  // Q5_K 83 -> 73 us, Q8_0 135 -> 117 us; Q6_K (whose 2-aligned blocks take
+  // 12-byte loads) and the down GEMMs (one wave per workgroup) measured
+  // slower with them and load in MFMA order.
+  constexpr bool CO = EPI == KQ_GATEUP && FMT != KQ_Q6_K;
+  const int r16c = lane >> 2, kcc = lane & 3;
+  const int psrc = (4 * r16 + kc) * 4;
   const int nsb = g.kdim / kQK;
 
   // activation row of this lane's A operand, and of its 4 C rows
@@ -532,7 +586,7 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
     }
     return (a >= 0 && a < g.a_rows) ? a : -1;
   };
-  const int arow = act_row(r16);
+  const int arow = act_row(r16), arow_c = act_row(r16c);
   int crow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) crow[i] = act_row(kc * 4 + i);
@@ -549,13 +603,15 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
 
   // byte offsets (unit 0) of this lane's weight rows: fragment f is column
   // group f / 2 (gate-up: f even gate, f odd up) or f (down)
-  uint32_t wrow[NB];
+  uint32_t wrow[NB], wrow_c[NB];
 #pragma unroll
   for (int f = 0; f < NB; ++f) {
     const int fo = (EPI == KQ_GATEUP) ? (f >> 1) : f;
-    const int c = col0 + fo * 16 + r16;
+    const int c = col0 + fo * 16 + r16, cc = col0 + fo * 16 + r16c;
     const int wr = (EPI == KQ_GATEUP && (f & 1)) ? g.n_out + c : c;
+    const int wrc = (EPI == KQ_GATEUP && (f & 1)) ? g.n_out + cc : cc;
     wrow[f] = (c < g.n_out) ? (uint32_t)(wr * row_bytes) : kqOob;
+    wrow_c[f] = (cc < g.n_out) ? (uint32_t)(wrc * row_bytes) : kqOob;
   }
 
   float acc[NB][4];
@@ -569,7 +625,7 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
   const int u0 = min(nsb, wave * per), u1 = min(nsb, u0 + per);
   for (int u = u0; u < u1; ++u) {
     KqA<FMT> a;
-    kq_aload<FMT>(a, g, rq, rd, rs, arow, crow, u, kc);
+    kq_aload<FMT, CO>(a, g, rq, rd, rs, arow, crow, u, kc, arow_c, kcc, psrc);
     // Q6_K: activation operands restricted to k 0-15 / 16-31 of each group
     long alo[8], ahi[8];
     if constexpr (FMT == KQ_Q6_K) {
@@ -581,7 +637,9 @@ __global__ __launch_bounds__(64 * KS) void kq_stream_kernel(KqArgs g) {
     }
     KqW<FMT> w[NB];
 #pragma unroll
-    for (int f = 0; f < NB; ++f) kq_wload<FMT>(w[f], rw, wrow[f] + (uint32_t)u * UB, kc);
+    for (int f = 0; f < NB; ++f)
+      kq_wload<FMT, CO>(w[f], rw, wrow[f] + (uint32_t)u * UB, kc, wrow_c[f] + (uint32_t)u * UB,
+                        kcc, psrc);
 #pragma unroll
     for (int f = 0; f < NB; ++f) {
       // one fragment at a time: keeps the MFMA results of only one
