@@ -22,7 +22,7 @@
 // ceil(P/BM) + min(E, P) on the number of slots; surplus workgroups leave at
 // once.
 //
-// Three kernel shapes, picked on the host by rows per expert and tile count:
+// Three kernels, picked on the host by rows per expert and tile count:
 //  * stream_kernel (few rows per expert: decode, many small experts, a dense
 //    shared expert of a few hundred rows): a workgroup owns a 16- or 32-row
 //    block of one expert and 16..64 output columns; its waves split the k
@@ -31,14 +31,17 @@
 //    with no LDS staging and no barrier in the k loop; the partial tiles meet
 //    once in LDS, added in a fixed order. The small work units keep every CU
 //    streaming to the end. HBM-bound by design.
-//  * tiled_dma_kernel (gate-up with hundreds of rows per expert): 320 x 256
-//    block tile on 8 waves, k step 64, a 2-stage LDS ring filled by
-//    direct-to-LDS buffer loads, XOR-swizzled rows, v_mfma_f32_32x32x16_bf16;
-//    the 32-row fragments past a tile's last row are skipped.
-//  * tiled_kernel (down with hundreds of rows per expert): 128 x 128 block
-//    tile, 4 waves of 64 x 64, k step 64 staged through LDS with padded rows
-//    (conflict-free 16-byte reads), register prefetch of the next k step
-//    during the MFMAs, 4 workgroups per CU.
+//  * tiled_dma_kernel (gate-up and down with hundreds of rows per expert):
+//    320 x 256 block tile on 8 waves (128 x 128 for a gate-up with too few
+//    320-row tiles to fill the chip), k step 64, a 2-stage LDS ring filled by
+//    direct-to-LDS buffer loads that four producer waves issue,
+//    XOR-swizzled rows, v_mfma_f32_32x32x16_bf16, blocks regrouped by XCD;
+//    the 32-row fragments past a tile's last row are skipped; the gate-up's
+//    SiLU comes from a table that the stage past the end of k loads.
+//  * tiled_kernel (a down GEMM with too few 320 x 256 tiles: an owner's
+//    share): 128 x 128 block tile, 4 waves of 64 x 64, k step 64 staged
+//    through LDS with padded rows (conflict-free 16-byte reads), register
+//    prefetch of the next k step during the MFMAs, 4 workgroups per CU.
 //
 // Epilogues (all per element, f32, no contraction):
 //  * gate-up: the block loads the gate rows [n, n+16) / [n, n+32) and the
