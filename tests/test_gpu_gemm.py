@@ -108,9 +108,14 @@ def test_tiled_gemms_bit_exact_on_exact_arithmetic(gpu_lib, skew):
     assert_bits_equal(bits(eo), O.down_proj(a2, wd, sp, off, w.reshape(-1)), "expert_out")
 
 
-@pytest.mark.parametrize("T,H,I", [(16, 64, 32), (512, 264, 72), (40, 128, 512)])
+@pytest.mark.parametrize("T,H,I", [(16, 64, 32), (512, 264, 72), (40, 128, 512),
+                                   (16384, 136, 2560), (16384, 2816, 72)])
 def test_identity_rows_bit_exact(gpu_lib, T, H, I):
-    """NULL sorted_pairs/offsets: a dense expert (the shared expert)."""
+    """NULL sorted_pairs/offsets: a dense expert (the shared expert). The two
+    16384-row cases take the tile kernels' one-expert block order: the first
+    the 320 x 256 direct-load gate-up and the register-staged 128 x 128 down,
+    the second the 128 x 128 direct-load gate-up and the 320 x 256 down."""
+    print(f"identity rows T={T} H={H} I={I}", flush=True)
     x = _exact_bf16(T + H, (T, H), -4, 4, 1.0)
     wgu = _exact_bf16(I + 1, (1, 2 * I, H), -4, 4, 2.0 ** -6)
     act = gpu_lib.moe_grouped_gemm_gateup_silu(to_dev_bf16(x), packed_gu(wgu), None, None, 1)
