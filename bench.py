@@ -104,7 +104,7 @@ def algorithmic_work(cfg, offsets):
     return gu, dn, touched
 
 
-KERNEL_CODE_FILES = ("gemm.hip", "device_math.h", "lds_dma.h", "silu_table.h")
+KERNEL_CODE_FILES = ("gemm.hip", "device_math.h", "launch.h", "lds_dma.h", "silu_table.h")
 
 
 def kernel_code_fingerprint():

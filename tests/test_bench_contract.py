@@ -32,6 +32,29 @@ def test_multi_gpu_refused():
     assert "one GPU" in msg["error"]
 
 
+def test_kernel_fingerprint_covers_every_local_header():
+    """roofline.traffic is reported only while the GEMM kernel code matches the
+    fingerprint recorded with the counters; the fingerprint must cover
+    gemm.hip and every header of the library that it includes, so a change in
+    any of them drops the stale traffic figure."""
+    import re
+    sys.path.insert(0, ROOT)
+    import bench
+    csrc = os.path.join(ROOT, "mixture_experts_ffn_expert_amd", "csrc")
+    seen, todo = set(), ["gemm.hip"]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        seen.add(name)
+        for inc in re.findall(r'#include\s+"([^"]+)"', open(os.path.join(csrc, name)).read()):
+            if os.path.exists(os.path.join(csrc, inc)):
+                todo.append(inc)
+    assert seen == set(bench.KERNEL_CODE_FILES), (sorted(seen), bench.KERNEL_CODE_FILES)
+    a = bench.kernel_code_fingerprint()
+    assert len(a) == 64 and a == bench.kernel_code_fingerprint()
+
+
 def test_algorithmic_work_formulas():
     sys.path.insert(0, ROOT)
     import bench
