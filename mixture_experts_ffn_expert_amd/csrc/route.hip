@@ -12,13 +12,14 @@
 //   lowest expert id holding it, so ties go to the lower id; lane k keeps the
 //   k-th logit, computes e_k = exp(l_k - l_0), every lane forms the same
 //   sequential f32 sum, lane k divides.
-// Grouping (group_kernel for up to 4096 pairs, else the count / scan /
-//   scatter kernels over 1024-pair segments): (i) per-wave expert histograms
-//   in LDS, (ii) an exclusive scan over experts (and segments) gives every
-//   wave its first output position per expert, (iii) each wave walks its part
-//   in order, 64 pairs at a time, ranks equal experts inside the 64 by
-//   ballots, and scatters. No atomic decides an order, so the permutation is
-//   the stable one and is reproducible.
+// Grouping (group_kernel for up to 4096 pairs, else the count kernel over
+//   1024-pair segments followed by the scan and the scatter, in one launch
+//   where the count table is small): (i) per-wave expert histograms in LDS,
+//   (ii) an exclusive scan over experts (and segments) gives every wave its
+//   first output position per expert, (iii) each wave walks its part in
+//   order, 64 pairs at a time, ranks equal experts inside the 64 by ballots,
+//   and scatters. No atomic decides an order, so the permutation is the
+//   stable one and is reproducible.
 #include <mutex>
 
 #include "device_math.h"
@@ -332,24 +333,66 @@ constexpr int kGroupSeg = 4096;
 // shape, mostly in the scatter's serial walk).
 constexpr int kScatterSeg = 1024;
 
-// Stable in-order scatter of pairs [beg, end) by one workgroup. cur[w][e]
-// holds, on entry, wave w's first output position for expert e; wave w owns
-// the w-th contiguous part of the segment and walks it 64 pairs at a time,
-// ranking equal experts inside the 64 with ballots over the id bits.
-__device__ __forceinline__ void scatter_segment(const int32_t* ids, int beg, int end,
-                                                int E, int (*cur)[kMaxE],
-                                                int32_t* __restrict__ sorted) {
+// Items per lane of a wave's part: a segment of n pairs gives each of the
+// kGroupWaves waves a contiguous part of ceil(n / kGroupWaves) pairs, 64 per
+// item.
+constexpr int kGroupItems = kGroupSeg / kGroupWaves / 64;      // 8
+constexpr int kScatterItems = kScatterSeg / kGroupWaves / 64;  // 2
+static_assert(kGroupItems * 64 * kGroupWaves == kGroupSeg &&
+              kScatterItems * 64 * kGroupWaves == kScatterSeg, "parts of whole items");
+
+// The expert ids of wave w's part [wb, we) of segment [beg, end): item j of
+// lane l is pair wb + 64 j + l (-1 past the part). All loads are issued
+// before the first is used, and the ids stay in registers for both the count
+// and the scatter.
+template <int NI>
+__device__ __forceinline__ void load_part(const int32_t* ids, int beg, int end, int& wb, int& we,
+                                          int (&v)[NI]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int seg = (end - beg + kGroupWaves - 1) / kGroupWaves;
-  const int wb = min(end, beg + wave * seg);
-  const int we = min(end, wb + seg);
+  wb = min(end, beg + wave * seg);
+  we = min(end, wb + seg);
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int p = wb + 64 * j + lane;
+    v[j] = (p < we) ? ids[p] : -1;
+  }
+}
+
+// Per-wave expert counts of the waves' parts: cur[w][e] for e < E (entries
+// past E are not touched). Counts commute, so LDS atomics are fine here.
+template <int NI>
+__device__ __forceinline__ void count_part(const int (&v)[NI], int E, int (*cur)[kMaxE]) {
+  const int wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) cur[w][e] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NI; ++j)
+    if ((unsigned)v[j] < (unsigned)E) atomicAdd(&cur[wave][v[j]], 1);
+  __syncthreads();
+}
+
+// Stable in-order scatter of the wave's part. cur[w][e] holds, on entry, wave
+// w's first output position for expert e; the wave walks its part 64 pairs
+// at a time, ranking equal experts inside the 64 with ballots over the id
+// bits.
+template <int NI>
+__device__ __forceinline__ void scatter_part(const int (&v)[NI], int wb, int we, int E,
+                                             int (*cur)[kMaxE], int32_t* __restrict__ sorted) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  for (int base = wb; base < we; base += 64) {
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int base = wb + 64 * j;
+    if (base >= we) break;  // uniform over the wave
     const int p = base + lane;
-    int e = (p < we) ? ids[p] : 0;
-    const bool valid = p < we && (unsigned)e < (unsigned)E;  // ids come from topk_kernel
+    int e = v[j];
+    const bool valid = p < we && (unsigned)e < (unsigned)E;  // ids come from the top-k kernels
     if (!valid) e = 0;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
@@ -368,44 +411,20 @@ __device__ __forceinline__ void scatter_segment(const int32_t* ids, int beg, int
   }
 }
 
-// Per-wave expert counts of the waves' parts of segment [beg, end).
-__device__ __forceinline__ void count_segment(const int32_t* ids, int beg, int end,
-                                              int E, int (*cur)[kMaxE]) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < kGroupWaves * kMaxE; i += blockDim.x) (&cur[0][0])[i] = 0;
-  __syncthreads();
-  const int seg = (end - beg + kGroupWaves - 1) / kGroupWaves;
-  const int wb = min(end, beg + wave * seg);
-  const int we = min(end, wb + seg);
-  // counts commute, so LDS atomics are fine here
-  for (int p = wb + lane; p < we; p += 64) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cur[wave][e], 1);
-  }
-  __syncthreads();
-}
-
-// Single workgroup (kGroupWaves waves): counts, the exclusive scan over
-// experts, then the scatter. cur: per-wave counts, then per-wave cursors.
-__device__ __forceinline__ void group_block(const int32_t* __restrict__ ids, int P, int E,
-                                            int32_t* __restrict__ offsets,
-                                            int32_t* __restrict__ sorted, int (*cur)[kMaxE],
-                                            int* wave_tot) {
+// Exclusive scan of tot[e] over experts e < E by the whole workgroup: thread
+// i owns experts [e0, e1) = [i*per, (i+1)*per) in order and gets the first
+// position of expert e0; the next owned expert starts tot[e] later.
+__device__ __forceinline__ int scan_experts(int E, const int* tot, int* wave_tot, int& e0,
+                                            int& e1) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  count_segment(ids, 0, P, E, cur);
-
-  // totals per expert and their exclusive scan; thread i owns experts
-  // [i*per, (i+1)*per) in order
   const int nthreads = kGroupWaves * 64;
   const int per = (E + nthreads - 1) / nthreads;
-  const int e0 = min(E, tid * per);
-  const int e1 = min(E, e0 + per);
+  e0 = min(E, tid * per);
+  e1 = min(E, e0 + per);
   int local = 0;
-  for (int e = e0; e < e1; ++e)
-    for (int w = 0; w < kGroupWaves; ++w) local += cur[w][e];
+  for (int e = e0; e < e1; ++e) local += tot[e];
   int incl = local;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
@@ -416,26 +435,43 @@ __device__ __forceinline__ void group_block(const int32_t* __restrict__ ids, int
   __syncthreads();
   int run = incl - local;
   for (int w = 0; w < wave; ++w) run += wave_tot[w];
+  return run;
+}
+
+// Single workgroup (kGroupWaves waves, P <= kGroupSeg): counts, the
+// exclusive scan over experts, then the scatter.
+__global__ __launch_bounds__(kGroupWaves * 64) void group_kernel(const int32_t* __restrict__ ids,
+                                                                 int P, int E,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ sorted) {
+  __shared__ int cur[kGroupWaves][kMaxE];  // per-wave counts, then per-wave cursors
+  __shared__ int tot[kMaxE];
+  __shared__ int wave_tot[kGroupWaves];
+  int v[kGroupItems];
+  int wb, we;
+  load_part(ids, 0, P, wb, we, v);
+  count_part(v, E, cur);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) n += cur[w][e];
+    tot[e] = n;
+  }
+  __syncthreads();
+  int e0, e1;
+  int run = scan_experts(E, tot, wave_tot, e0, e1);
   for (int e = e0; e < e1; ++e) {
     offsets[e] = run;
+#pragma unroll
     for (int w = 0; w < kGroupWaves; ++w) {
       const int n = cur[w][e];
       cur[w][e] = run;  // cursor of wave w for expert e
       run += n;
     }
   }
-  if (tid == 0) offsets[E] = P;
+  if (threadIdx.x == 0) offsets[E] = P;
   __syncthreads();
-  scatter_segment(ids, 0, P, E, cur, sorted);
-}
-
-__global__ __launch_bounds__(kGroupWaves * 64) void group_kernel(const int32_t* __restrict__ ids,
-                                                                 int P, int E,
-                                                                 int32_t* __restrict__ offsets,
-                                                                 int32_t* __restrict__ sorted) {
-  __shared__ int cur[kGroupWaves][kMaxE];
-  __shared__ int wave_tot[kGroupWaves];
-  group_block(ids, P, E, offsets, sorted, cur, wave_tot);
+  scatter_part(v, wb, we, E, cur, sorted);
 }
 
 // Multi-workgroup grouping, step 1: expert counts of each segment of
@@ -445,7 +481,10 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_count_kernel(
   __shared__ int cur[kGroupWaves][kMaxE];
   const int beg = blockIdx.x * kScatterSeg;
   const int end = min(P, beg + kScatterSeg);
-  count_segment(ids, beg, end, E, cur);
+  int v[kScatterItems];
+  int wb, we;
+  load_part(ids, beg, end, wb, we, v);
+  count_part(v, E, cur);
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int n = 0;
 #pragma unroll
@@ -501,17 +540,13 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(int32_t* __restrict__ 
   if (tid == 0) offsets[E] = P;
 }
 
-// Step 3: each segment scatters its pairs in order from its own positions.
-__global__ __launch_bounds__(kGroupWaves * 64) void group_scatter_kernel(
-    const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ base,
-    int32_t* __restrict__ sorted) {
-  __shared__ int cur[kGroupWaves][kMaxE];
-  const int beg = blockIdx.x * kScatterSeg;
-  const int end = min(P, beg + kScatterSeg);
-  count_segment(ids, beg, end, E, cur);
-  // wave w's cursor = segment base + counts of waves before w (in order)
+// Wave cursors from a segment's base positions: on entry cur[w][e] holds
+// wave w's count of expert e; on return its first output position, base[e] +
+// the counts of the waves before w (in order). base_of(e) gives base[e].
+template <typename Base>
+__device__ __forceinline__ void wave_cursors(int E, int (*cur)[kMaxE], Base base_of) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = base[(size_t)blockIdx.x * E + e];
+    int run = base_of(e);
 #pragma unroll
     for (int w = 0; w < kGroupWaves; ++w) {
       const int n = cur[w][e];
@@ -520,7 +555,82 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_scatter_kernel(
     }
   }
   __syncthreads();
-  scatter_segment(ids, beg, end, E, cur, sorted);
+}
+
+// Step 3: each segment scatters its pairs in order from its own positions.
+__global__ __launch_bounds__(kGroupWaves * 64) void group_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ base,
+    int32_t* __restrict__ sorted) {
+  __shared__ int cur[kGroupWaves][kMaxE];
+  const int beg = blockIdx.x * kScatterSeg;
+  const int end = min(P, beg + kScatterSeg);
+  int v[kScatterItems];
+  int wb, we;
+  load_part(ids, beg, end, wb, we, v);
+  count_part(v, E, cur);
+  const int32_t* seg_base = base + (size_t)blockIdx.x * E;
+  wave_cursors(E, cur, [=](int e) { return seg_base[e]; });
+  scatter_part(v, wb, we, E, cur, sorted);
+}
+
+// Steps 2 and 3 in one launch, for count tables of at most kFoldCounts
+// entries: every segment's workgroup reads the whole table cnt[b][e] (coalesced,
+// up to kFoldLoads loads per thread in flight at once), sums each expert's
+// total and the counts of the segments before its own, scans the totals, and
+// scatters from its own positions; workgroup 0 also writes the offsets. The
+// table is only read, so the workgroups do not depend on one another.
+constexpr int kFoldLoads = 16;
+constexpr int kFoldCounts = kFoldLoads * kGroupWaves * 64 * 2;  // 16,384
+__global__ __launch_bounds__(kGroupWaves * 64) void group_scan_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ cnt, int nseg,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted) {
+  __shared__ int cur[kGroupWaves][kMaxE];
+  __shared__ int tot[kMaxE];
+  __shared__ int pre[kMaxE];
+  __shared__ int wave_tot[kGroupWaves];
+  const int tid = threadIdx.x;
+  constexpr int NT = kGroupWaves * 64;
+  const int seg = blockIdx.x;
+  const int beg = seg * kScatterSeg;
+  const int end = min(P, beg + kScatterSeg);
+  int v[kScatterItems];
+  int wb, we;
+  load_part(ids, beg, end, wb, we, v);
+  for (int e = tid; e < E; e += NT) {
+    tot[e] = 0;
+    pre[e] = 0;
+  }
+  count_part(v, E, cur);  // its barriers also order the zeroing above
+  const int n = E * nseg;
+  for (int i0 = 0; i0 < n; i0 += NT * kFoldLoads) {
+    int c[kFoldLoads];
+#pragma unroll
+    for (int j = 0; j < kFoldLoads; ++j) {
+      const int i = i0 + j * NT + tid;
+      c[j] = (i < n) ? cnt[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kFoldLoads; ++j) {
+      const int i = i0 + j * NT + tid;
+      if (c[j] != 0) {  // i < n
+        const int b = i / E, e = i - b * E;
+        atomicAdd(&tot[e], c[j]);  // integer sums: the order does not matter
+        if (b < seg) atomicAdd(&pre[e], c[j]);
+      }
+    }
+  }
+  __syncthreads();
+  int e0, e1;
+  int run = scan_experts(E, tot, wave_tot, e0, e1);
+  for (int e = e0; e < e1; ++e) {
+    if (seg == 0) offsets[e] = run;
+    pre[e] += run;  // the segment's first position for expert e
+    run += tot[e];
+  }
+  if (seg == 0 && tid == 0) offsets[E] = P;
+  __syncthreads();
+  wave_cursors(E, cur, [&](int e) { return pre[e]; });
+  scatter_part(v, wb, we, E, cur, sorted);
 }
 
 size_t route_workspace_bytes(int T, int E, int K) {
@@ -541,9 +651,14 @@ static hipError_t launch_grouping(const int32_t* ids, int P, int E, int32_t* off
     int32_t* cnt = static_cast<int32_t*>(ws);
     hipLaunchKernelGGL(group_count_kernel, dim3(nseg), dim3(kGroupWaves * 64), 0, s, ids, P, E,
                        cnt);
-    hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, nseg, P, E, offsets);
-    hipLaunchKernelGGL(group_scatter_kernel, dim3(nseg), dim3(kGroupWaves * 64), 0, s, ids, P, E,
-                       cnt, sorted);
+    if ((long long)nseg * E <= kFoldCounts) {
+      hipLaunchKernelGGL(group_scan_scatter_kernel, dim3(nseg), dim3(kGroupWaves * 64), 0, s, ids,
+                         P, E, cnt, nseg, offsets, sorted);
+    } else {
+      hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, nseg, P, E, offsets);
+      hipLaunchKernelGGL(group_scatter_kernel, dim3(nseg), dim3(kGroupWaves * 64), 0, s, ids, P,
+                         E, cnt, sorted);
+    }
   }
   return hipGetLastError();
 }
