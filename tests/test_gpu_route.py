@@ -62,10 +62,13 @@ def test_route_is_deterministic(gpu_lib):
 
 
 @pytest.mark.parametrize("T,E,K", [(513, 128, 8), (512, 128, 8), (3000, 1024, 32), (8192, 256, 8),
-                                   (4100, 128, 8), (640, 64, 7)])
+                                   (8200, 256, 8), (4100, 128, 8), (640, 64, 7), (2048, 1024, 8)])
 def test_route_multi_segment_grouping_with_dirty_workspace(gpu_lib, T, E, K):
     """Pair counts around the single-workgroup limit (4096 pairs) and far above
-    it (1024-pair segments, a partial last one); the caller's
+    it (1024-pair segments, a partial last one), on both sides of the largest
+    count table (segments x experts = 16,384) whose scan runs inside the
+    scatter launch: 8192 x 256 x 8 and 2048 x 1024 x 8 (more experts than
+    threads) at it, 8200 x 256 x 8 just past it; the caller's
     workspace starts full of garbage and the result must not depend on it."""
     g = np.random.Generator(np.random.PCG64(T + E + K))
     l = g.standard_normal((T, E)).astype(F32)
